@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module holds none of the attention arithmetic: it only draws inputs.
+Both the HIP path's tests/benchmark and the CPU oracle take their inputs from
+here, so the two sides always see the same bits.
+
+Recipe: ``g = torch.Generator('cpu').manual_seed(seed)``; Q, then K, then V,
+each drawn as ``torch.randn(shape, generator=g, dtype=float32) * sigma`` and
+rounded to bf16 (round-to-nearest-even, torch's cast).  Shapes are BHSD,
+row-major: Q [B, Hq, Sq, D], K [B, Hkv, Sk, D], V [B, Hkv, Sk, Dv].
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4"
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    Dv: int
+    sigma: float
+    seed: int
+    causal: bool
+    num_splits: int = 0  # decode only; 0 = the library's heuristic
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.D)
+
+    def shapes(self):
+        return ((self.B, self.Hq, self.Sq, self.D), (self.B, self.Hkv, self.Sk, self.D),
+                (self.B, self.Hkv, self.Sk, self.Dv))
+
+    def visible_pairs_per_head(self) -> int:
+        """Number of (query, key) pairs that take part, per (b, h)."""
+        if not self.causal:
+            return self.Sq * self.Sk
+        return sum(min(self.Sk, i + 1 + self.Sk - self.Sq) for i in range(self.Sq))
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: 2*D per score for QK^T plus 2*Dv per score for PV."""
+        return 2 * (self.D + self.Dv) * self.B * self.Hq * self.visible_pairs_per_head()
+
+    def bytes(self) -> int:
+        """Algorithmic HBM bytes: Q, K and V read once, O (bf16) and LSE (fp32)
+        written once; the NVFP4 workload adds the codes, scales and the global
+        scale."""
+        q = self.B * self.Hq * self.Sq * self.D
+        kv = self.B * self.Hkv * self.Sk * (self.D + self.Dv)
+        o = self.B * self.Hq * self.Sq * self.Dv
+        n = 2 * (q + kv + o) + 4 * self.B * self.Hq * self.Sq
+        if self.kind == "decode_nvfp4":
+            n += o // 2 + o // 16 + 4
+        return n
+
+    def kv_bytes(self) -> int:
+        return 2 * self.B * self.Hkv * self.Sk * (self.D + self.Dv)
+
+
+def default_scale(D: int) -> float:
+    """fp32 round-to-nearest of 1/sqrt(D), computed in double."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_tile_d16", "fwd", 1, 1, 1, 128, 128, 16, 16, 1.0, 0, False,
+                 note="one 128x128 score tile, head dim 16"),
+        Workload("prefill_causal_d64", "fwd", 4, 16, 16, 2048, 2048, 64, 64, 1.0, 1, True,
+                 note="causal prefill, 128x128 tiles"),
+        Workload("decode_gqa_d64", "decode", 64, 32, 8, 1, 8192, 64, 64, 1.0, 2, False,
+                 num_splits=16, note="GQA 4:1 decode, 16 KV splits"),
+        Workload("decode_mqa_d512", "decode", 32, 64, 1, 1, 16384, 512, 512, 0.5, 3, False,
+                 note="all 64 query heads share one KV head, head dim 512"),
+        Workload("decode_nvfp4_d128", "decode_nvfp4", 128, 16, 16, 1, 4096, 128, 128, 1.0, 4,
+                 False, num_splits=1, note="MHA decode, O quantised to NVFP4"),
+    ]
+}
+
+
+def make_qkv(B, Hq, Hkv, Sq, Sk, D, Dv=None, *, sigma=1.0, seed=0):
+    """Q, K, V as contiguous bf16 CPU tensors drawn from one seeded generator."""
+    Dv = D if Dv is None else Dv
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    out = []
+    for shape in ((B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, Dv)):
+        t = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            t.mul_(sigma)
+        out.append(t.to(torch.bfloat16).contiguous())
+        del t
+    return tuple(out)
+
+
+def make_workload_inputs(w: Workload):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.Dv, sigma=w.sigma, seed=w.seed)
+
+
+def sample_rows(total: int, n: int, seed: int = 1234) -> np.ndarray:
+    """A seeded, sorted sample of flat row ids (always including the first and
+    last row), for checking full-size outputs one row at a time."""
+    rng = np.random.default_rng(seed)
+    n = min(n, total)
+    pick = rng.choice(total, size=n, replace=False)
+    pick[0] = 0
+    if n > 1:
+        pick[1] = total - 1
+    return np.unique(pick).astype(np.int64)
