@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: for the prefill workload one fmha_fwd call; for the
+decode workloads fmha_decode_splitkv (split kernel + log-sum-exp combine); for
+the NVFP4 workload the decode with the amax folded in plus nvfp4_quantize.
+
+The headline line is the causal prefill (B=4, H=16, S=2048, D=64) in TFLOP/s;
+the line also carries, under "workloads", every named workload (time per step,
+TFLOP/s, KV GB/s and fraction of the bound) and a "roofline" object for the
+headline kernel, timed with HIP events on the stream it runs on, plus the CPU
+oracle timed on a bounded sample of the same workload ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "FMHA TFLOP/s (prefill) and KV GB/s (decode) at hd=64/512 on 1 MI355X"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_causal_d64")
+    ap.add_argument("--only", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Runner:
+    """Device buffers and the step function of one workload."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import decode_fmha_fwd_amd as F
+        from workloads import make_workload_inputs
+
+        self.w, self.F, self.torch = w, F, torch
+        q, k, v = make_workload_inputs(w)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        self.ws = None
+        self.ws_bytes = 0
+        if w.kind != "fwd":
+            self.ws_bytes = F.fmha_decode_splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D,
+                                                                 w.num_splits)
+            if self.ws_bytes:
+                self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        if w.kind == "decode_nvfp4":
+            rows = w.B * w.Hq * w.Sq
+            self.rows = rows
+            self.amax = torch.zeros(1, dtype=torch.float32, device=dev)
+            self.codes = torch.empty((rows, w.Dv // 2), dtype=torch.uint8, device=dev)
+            self.scales = torch.empty((rows, w.Dv // 16), dtype=torch.uint8, device=dev)
+            self.gscale = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def step(self):
+        w, F = self.w, self.F
+        if w.kind == "fwd":
+            F.fmha_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D,
+                       w.scale, w.causal)
+        elif w.kind == "decode":
+            F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
+                                  w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws, self.ws_bytes)
+        else:
+            self.amax.zero_()
+            F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
+                                  w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws, self.ws_bytes,
+                                  self.amax)
+            F.nvfp4_quantize(self.o, self.rows, w.Dv, self.codes, self.scales, self.gscale,
+                             self.amax, None, 0)
+
+    def free(self):
+        for n in ("q", "k", "v", "o", "lse", "ws"):
+            setattr(self, n, None)
+
+
+def time_workload(w, dev, steps, warmup):
+    import torch
+    r = Runner(w, dev)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        r.step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[steps])
+    r.free()
+    del r
+    torch.cuda.empty_cache()
+    return total_ms / steps, per, wall
+
+
+def summarise(w, ms):
+    s = ms / 1e3
+    kv = w.kv_bytes()
+    out = {"workload": w.name, "ms_per_step": round(ms, 5),
+           "tflops": round(w.flops() / s / 1e12, 2),
+           "kv_gbs": round(kv / s / 1e9, 1),
+           "alg_gbs": round(w.bytes() / s / 1e9, 1)}
+    if w.kind == "fwd" and w.Sq > 1:
+        out["bound"] = "mfma"
+        out["frac_of_bound"] = round(out["tflops"] / BF16_PEAK_TFLOPS, 4)
+    else:
+        out["bound"] = "hbm"
+        out["frac_of_bound"] = round(out["alg_gbs"] / HBM_PEAK_GBS, 4)
+    return out
+
+
+def cpu_baseline(w, target_s):
+    """The fp64 oracle on a bounded, seeded sample of the workload's rows."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_workload_inputs, sample_rows
+
+    q, k, v = make_workload_inputs(w)
+    qa = q.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    ka = k.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    va = v.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    total = w.B * w.Hq * w.Sq
+
+    def vis(rows):
+        i = rows % w.Sq
+        if not w.causal:
+            return np.full(rows.shape, w.Sk, dtype=np.int64)
+        return np.minimum(w.Sk, i + 1 + w.Sk - w.Sq)
+
+    def run(n):
+        rows = sample_rows(total, n, seed=99)
+        t0 = time.perf_counter()
+        oracle.attention(qa, ka, va, B=w.B, Hq=w.Hq, Hkv=w.Hkv, Sq=w.Sq, Sk=w.Sk, D=w.D, Dv=w.Dv,
+                         scale=w.scale, causal=w.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        flops = float(2 * (w.D + w.Dv) * vis(rows).sum())
+        return rows.size, dt, flops
+
+    n, dt, fl = run(64)
+    n2 = int(min(total, max(64, n * target_s / max(dt, 1e-3))))
+    if n2 > n:
+        n, dt, fl = run(n2)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {total} query rows of {w.name} (seeded sample), fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the split-KV "
+              "decode and prefill shard over independent (batch, head) units with no exchange, "
+              "so multi-GPU figures are not produced here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    head = WORKLOADS[args.workload]
+    names = [head.name] + ([] if args.only else [n for n in WORKLOADS if n != head.name])
+    results = {}
+    for n in names:
+        w = WORKLOADS[n]
+        steps = args.steps
+        ms, per, wall = time_workload(w, dev, steps, args.warmup)
+        results[n] = (ms, per, summarise(w, ms))
+        print(f"# {n}: {ms:.4f} ms/step  {results[n][2]}", file=sys.stderr, flush=True)
+
+    ms, per, s = results[head.name]
+    kernel_ms = sorted(per)[len(per) // 2]
+    if head.kind == "fwd":
+        achieved = head.flops() / (kernel_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "attn_fwd_kernel<64,32,4,64,causal>", "kernel_ms_median": round(kernel_ms, 5)}
+        value, unit = s["tflops"], "TFLOP/s"
+    else:
+        achieved = head.bytes() / (kernel_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel_ms_median": round(kernel_ms, 5)}
+        value, unit = s["kv_gbs"], "GB/s"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": head.name, "B": head.B, "Hq": head.Hq, "Hkv": head.Hkv,
+                   "Sq": head.Sq, "Sk": head.Sk, "D": head.D, "causal": head.causal,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": [results[n][2] for n in names],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,458 @@
+// attn_kernels.hpp -- the fused attention kernel (prefill and split-KV decode)
+// and the log-sum-exp combine kernel for gfx950.
+//
+// The parts follow the feature list on the page
+// "NVFP4-1.1_RAW_CUDA_CPP_APPROACH.md": QK product on the matrix cores, an
+// in-kernel softmax that rescales the output accumulator when the running
+// maximum moves, a loop over several KV tiles, the PV product, a correction
+// epilogue that divides by the softmax sum, and (on that page, "multi-CTA")
+// several workgroups per row over disjoint key ranges, merged by a separate
+// combine kernel.
+//
+// Design (gfx950, not a translation of the pages' Blackwell kernel):
+//   * A workgroup of NW waves owns NW*MT query rows that share one KV head
+//     (MT = 32 or 16 rows per wave).  Rows are the flattened (grouped head,
+//     position) pairs of that KV head, so GQA decode packs all Hq/Hkv heads of
+//     a KV head into one workgroup and each K/V byte is read once.
+//   * K and V tiles of KT keys are loaded with 16-byte coalesced global loads
+//     into registers, written to a double-buffered LDS tile whose 16-byte
+//     chunks are XOR-swizzled by row, and read back as MFMA operands.
+//   * Scores are computed transposed, S^T = K * Q^T (K is the A operand, Q^T
+//     the B operand held in registers), so each lane owns ONE query row and a
+//     set of keys: row max and row sum are in-lane plus one or two lane swaps.
+//   * The output is accumulated transposed too, O^T += V^T * P^T: the
+//     probabilities stay in registers in exactly the layout the MFMA B operand
+//     wants (keys are assigned to k-slots to match), and V^T comes from the LDS
+//     tile through the gfx950 transpose read ds_read_b64_tr_b16.
+//   * Online softmax in base 2: m is kept in units of log2, p = exp2(s*c - m)
+//     with c = scale*log2(e) folded into one FMA; the output rescale factor is
+//     exp2(m_old - m_new).
+#pragma once
+
+#include <climits>
+
+#include "fmha_device.hpp"
+
+namespace fmha {
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;          // bf16 output (no split)
+  float* lse;           // fp32 [rows] or null (no split)
+  float* o_part;        // fp32 [rows][nsplit][D] (split)
+  float* lse_part;      // fp32 [rows][nsplit]   (split)
+  float* o_amax;        // optional running max |O| (no split)
+  int Hkv;
+  int Sq;
+  int Sk;
+  int rows_per_kv;      // (Hq / Hkv) * Sq query rows share one KV head
+  int n_row_blocks;     // ceil(rows_per_kv / (NW * MT))
+  int nsplit;           // key ranges per (batch, KV head)
+  int split_len;        // keys per range, a multiple of KT
+  float scale_log2;     // scale * log2(e)
+};
+
+// XOR swizzle of the 16-byte chunk index within a K/V row so that the 16
+// lanes of one LDS read phase, which read the same logical chunk of 16
+// consecutive rows, hit 16 distinct 16-byte bank groups.
+template <int CPR>
+__device__ inline int swz(int row) {
+  if constexpr (CPR >= 16) {
+    return row & 15;
+  } else {
+    return (row / (16 / CPR)) & (CPR - 1);
+  }
+}
+
+// Element offset of (row, col) in a swizzled [rows][D] bf16 tile.
+template <int D>
+__device__ inline int tile_off(int row, int col) {
+  constexpr int CPR = D / 8;
+  return row * D + (((col >> 3) ^ swz<CPR>(row)) << 3) + (col & 7);
+}
+
+// Q^T fragments, the B operand of S^T = K Q^T: for contraction step s the
+// lane holds Q[row][s*kK + 8*kg + 0..7] (zeros past D).
+template <int D, int MT>
+__device__ inline void load_q_frags(const uint16_t* qrow, int kg,
+                                    bf16x8 (&qf)[(D + Mfma<MT>::kK - 1) / Mfma<MT>::kK]) {
+  constexpr int KSTEPS = (D + Mfma<MT>::kK - 1) / Mfma<MT>::kK;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int d0 = s * Mfma<MT>::kK + 8 * kg;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (d0 < D) raw = *(const u32x4*)(qrow + d0);
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// The QK product of one KV tile: S^T[key][query] for KBLK blocks of MT keys,
+// K read from the swizzled LDS tile as the A operand (lane holds
+// K[kb*MT + lane % MT][s*kK + 8*(lane / MT) + 0..7]).  The raw dot products
+// are returned; the softmax scale is applied by the caller.
+template <int D, int MT, int KBLK>
+__device__ inline void qk_scores(const uint16_t* ks,
+                                 const bf16x8 (&qf)[(D + Mfma<MT>::kK - 1) / Mfma<MT>::kK],
+                                 int lane, typename Mfma<MT>::Acc (&sacc)[KBLK]) {
+  using M = Mfma<MT>;
+  constexpr int KSTEPS = (D + M::kK - 1) / M::kK;
+  const int kg = lane / MT;
+#pragma unroll
+  for (int kb = 0; kb < KBLK; ++kb) {
+    sacc[kb] = typename M::Acc{};
+    const int krow = kb * MT + lane % MT;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int col = s * M::kK + 8 * kg;
+      u32x4 raw = lds_read_b128((const FMHA_LDS void*)&ks[tile_off<D>(krow, col < D ? col : 0)]);
+      sacc[kb] = M::run(__builtin_bit_cast(bf16x8, raw), qf[s], sacc[kb]);
+    }
+  }
+}
+
+template <int D, int MT, int NW, int KT, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
+  using M = Mfma<MT>;
+  using Acc = typename M::Acc;
+  constexpr int NT = NW * 64;
+  constexpr int CPR = D / 8;                       // 16-byte chunks per K/V row
+  constexpr int TILE_CHUNKS = KT * CPR;
+  constexpr int NCH = (TILE_CHUNKS + NT - 1) / NT; // chunks per thread per tensor
+  constexpr int KSTEPS = (D + M::kK - 1) / M::kK;  // QK contraction steps
+  constexpr int KBLK = KT / MT;                    // MT-key blocks per tile
+  constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
+  constexpr int ROWS_WG = NW * MT;
+  constexpr int NPV = (MT == 32) ? 2 * KBLK : KBLK / 2;  // PV instructions per d-block
+  static_assert(KT % MT == 0, "KT must be a multiple of MT");
+  static_assert(MT == 32 || KT % 32 == 0, "16-row waves consume 32 keys per PV step");
+  static_assert(D % 16 == 0 && CPR >= 2, "head dim must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][KT * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const int split = blockIdx.x / p.n_row_blocks;
+  int rb = blockIdx.x - split * p.n_row_blocks;
+  if (CAUSAL) rb = p.n_row_blocks - 1 - rb;  // longest key ranges start first
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+
+  const long long bh_kv = (long long)b * p.Hkv + kvh;
+  const uint16_t* __restrict__ kbase = p.k + bh_kv * p.Sk * D;
+  const uint16_t* __restrict__ vbase = p.v + bh_kv * p.Sk * D;
+  const long long row_base = bh_kv * p.rows_per_kv;  // flat (b, h, i) id of row 0
+
+  const int r_wg0 = rb * ROWS_WG;
+  const int r_wave0 = r_wg0 + wave * MT;
+  const int qcol = lane % MT;  // the query row this lane owns
+  const int kg = lane / MT;    // contraction lane group
+  const int my_r = r_wave0 + qcol;
+  const bool row_ok = my_r < p.rows_per_kv;
+  const int my_rc = row_ok ? my_r : p.rows_per_kv - 1;
+  const int diag = p.Sk - p.Sq;  // causal: key j visible to row i iff j <= i + diag
+
+  // Key range of this workgroup.
+  int kbeg = split * p.split_len;
+  int kend = min(p.Sk, kbeg + p.split_len);
+  int wave_min_last = INT_MAX;  // smallest last-visible key over the wave's rows
+  int wave_max_last = INT_MAX;  // largest
+  if (CAUSAL) {
+    const int r_end = min(p.rows_per_kv, r_wg0 + ROWS_WG) - 1;
+    const int i_last = (r_wg0 / p.Sq == r_end / p.Sq) ? r_end % p.Sq : p.Sq - 1;
+    kend = min(kend, i_last + diag + 1);
+    if (r_wave0 < p.rows_per_kv) {
+      const int rw_end = min(p.rows_per_kv, r_wave0 + MT) - 1;
+      const bool one_head = (r_wave0 / p.Sq == rw_end / p.Sq);
+      wave_min_last = (one_head ? r_wave0 % p.Sq : 0) + diag;
+      wave_max_last = (one_head ? rw_end % p.Sq : p.Sq - 1) + diag;
+    } else {
+      wave_min_last = wave_max_last = -1;
+    }
+  }
+  const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
+
+  bf16x8 qf[KSTEPS];
+  load_q_frags<D, MT>(p.q + (row_base + my_rc) * D, kg, qf);
+
+  Acc oacc[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) oacc[i] = Acc{};
+  float m_run = kNegBig;
+  float l_run = 0.0f;
+
+  u32x4 kreg[NCH], vreg[NCH];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + c * NT;
+      if (TILE_CHUNKS % NT == 0 || idx < TILE_CHUNKS) {
+        const int row = idx / CPR;
+        const int ch = idx - row * CPR;
+        const long long key = min(t0 + row, p.Sk - 1);  // ragged tail: clamp, masked later
+        kreg[c] = *(const u32x4*)(kbase + key * D + ch * 8);
+        vreg[c] = *(const u32x4*)(vbase + key * D + ch * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + c * NT;
+      if (TILE_CHUNKS % NT == 0 || idx < TILE_CHUNKS) {
+        const int row = idx / CPR;
+        const int ch = idx - row * CPR;
+        const int off = row * D + ((ch ^ swz<CPR>(row)) << 3);
+        lds_write_b128((FMHA_LDS void*)&smem[buf][0][off], kreg[c]);
+        lds_write_b128((FMHA_LDS void*)&smem[buf][1][off], vreg[c]);
+      }
+    }
+  };
+
+  const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
+  if (ntiles > 0) {
+    load_tile(kbeg);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = kbeg + it * KT;
+    const int buf = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(t0 + KT);
+
+    // Causal: a tile entirely past this wave's last visible key adds nothing.
+    const bool wave_active = !CAUSAL || t0 <= wave_max_last;
+    if (wave_active) {
+      const uint16_t* ks = &smem[buf][0][0];
+      const uint16_t* vs = &smem[buf][1][0];
+
+      // ---- S^T = K Q^T ----
+      Acc sacc[KBLK];
+      qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
+
+      // ---- mask the ragged end and the causal diagonal ----
+      const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int r = 0; r < M::kRegs; ++r) {
+            const int key = t0 + kb * MT + acc_row<MT>(lane, r);
+            if (key >= kend || key > my_last) sacc[kb][r] = -__builtin_inff();
+          }
+      }
+
+      // ---- online softmax (base 2) ----
+      float mloc = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::kRegs; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+      mloc = group_max<MT>(mloc);
+      const float m_new = fmaxf(m_run, mloc * p.scale_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < M::kRegs; ++r) {
+          const float pv = fast_exp2(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_new));
+          sacc[kb][r] = pv;
+          psum += pv;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+
+      // ---- O^T += V^T P^T ----
+      // Source-lane coordinates for the transpose read.
+      const int grp = lane >> 4;
+      const int tj = (lane >> 2) & 3;
+      const int ta = lane & 3;
+#pragma unroll
+      for (int step = 0; step < NPV; ++step) {
+        // Probabilities as the B operand: k-slot e of lane group g.
+        u32x4 pw;
+        int row1, row2;
+        if constexpr (MT == 32) {
+          const int kb = step >> 1, t2 = step & 1;
+          pw[0] = pack_bf16x2(sacc[kb][8 * t2 + 0], sacc[kb][8 * t2 + 1]);
+          pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
+          pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
+          pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
+          // k-slots 0..3 <-> keys kofs + 4h + 0..3, slots 4..7 <-> kofs + 8 + 4h + 0..3
+          row1 = kb * 32 + 16 * t2 + 4 * (grp >> 1) + tj;
+          row2 = row1 + 8;
+        } else {
+          const int kb0 = 2 * step, kb1 = 2 * step + 1;
+          pw[0] = pack_bf16x2(sacc[kb0][0], sacc[kb0][1]);
+          pw[1] = pack_bf16x2(sacc[kb0][2], sacc[kb0][3]);
+          pw[2] = pack_bf16x2(sacc[kb1][0], sacc[kb1][1]);
+          pw[3] = pack_bf16x2(sacc[kb1][2], sacc[kb1][3]);
+          // k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
+          row1 = 32 * step + 4 * grp + tj;
+          row2 = row1 + 16;
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
+          if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
+          const u32x2 lo = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row1, col)]);
+          const u32x2 hi = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row2, col)]);
+          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = M::run(__builtin_bit_cast(bf16x8, va), pb, oacc[db]);
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l, log-sum-exp ----
+  const float l_tot = group_sum<MT>(l_run);
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l_tot;
+  const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
+
+  float amax = 0.0f;
+  if (row_ok) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int qd = 0; qd < M::kRegs / 4; ++qd) {
+        const int d0 = (MT == 32) ? db * 32 + 8 * qd + 4 * kg : db * 16 + 4 * kg;
+        if (d0 >= D) continue;
+        const float o0 = oacc[db][4 * qd + 0] * inv, o1 = oacc[db][4 * qd + 1] * inv;
+        const float o2 = oacc[db][4 * qd + 2] * inv, o3 = oacc[db][4 * qd + 3] * inv;
+        if constexpr (SPLIT) {
+          float* dst = p.o_part + ((row_base + my_r) * p.nsplit + split) * D + d0;
+          *(f32x4*)dst = f32x4{o0, o1, o2, o3};
+        } else {
+          const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
+          *(u32x2*)(p.o + (row_base + my_r) * D + d0) = u32x2{w0, w1};
+          if (p.o_amax) {
+            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
+            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
+            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
+            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 >> 16)));
+          }
+        }
+      }
+    }
+    if (kg == 0) {
+      if constexpr (SPLIT) {
+        p.lse_part[(row_base + my_r) * p.nsplit + split] = lse_val;
+      } else if (p.lse) {
+        p.lse[row_base + my_r] = lse_val;
+      }
+    }
+  }
+  if constexpr (!SPLIT) {
+    if (p.o_amax) {
+      amax = wave_max(amax);
+      if (lane == 0) atomic_max_nonneg(p.o_amax, amax);
+    }
+  }
+}
+
+// Test hook: raw scores S = scale * Q K^T for Sq, Sk <= 128 of the first
+// (batch, head), through the same load_q_frags / qk_scores path as the
+// attention kernel (4 waves x 32 query rows, one 128-key tile).
+template <int D>
+__global__ __launch_bounds__(256) void qk_scores_debug_kernel(const uint16_t* q, const uint16_t* k,
+                                                              float* s_out, int Sq, int Sk,
+                                                              float scale) {
+  constexpr int MT = 32, KT = 128, KBLK = KT / MT, CPR = D / 8;
+  using Acc = typename Mfma<MT>::Acc;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[KT * D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int idx = tid; idx < KT * CPR; idx += 256) {
+    const int row = idx / CPR, ch = idx % CPR;
+    const int key = min(row, Sk - 1);
+    lds_write_b128((FMHA_LDS void*)&ks[row * D + ((ch ^ swz<CPR>(row)) << 3)],
+                   *(const u32x4*)(k + (long long)key * D + ch * 8));
+  }
+  __syncthreads();
+  const int qrow = wave * MT + lane % MT;
+  bf16x8 qf[(D + 15) / 16];
+  load_q_frags<D, MT>(q + (long long)min(qrow, Sq - 1) * D, lane / MT, qf);
+  Acc sacc[KBLK];
+  qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
+  if (qrow < Sq) {
+    for (int kb = 0; kb < KBLK; ++kb)
+      for (int r = 0; r < Mfma<MT>::kRegs; ++r) {
+        const int key = kb * MT + acc_row<MT>(lane, r);
+        if (key < Sk) s_out[(long long)qrow * Sk + key] = sacc[kb][r] * scale;
+      }
+  }
+}
+
+// Log-sum-exp combine of split results: one wave per query row.
+//   m = max_s lse_s;  LSE = m + log sum_s exp(lse_s - m);
+//   O = sum_s exp(lse_s - LSE) * O_s  -> bf16.
+// Splits with lse_s = -inf (no visible key) weigh 0.
+template <int D>
+__global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restrict__ o_part,
+                                                          const float* __restrict__ lse_part,
+                                                          uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse,
+                                                          float* __restrict__ o_amax,
+                                                          long long nrows, int nsplit) {
+  constexpr int VPL = D / 64;  // output elements per lane
+  static_assert(D % 64 == 0, "combine expects D a multiple of 64");
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const float* lp = lse_part + row * nsplit;
+
+  float m = -__builtin_inff();
+  for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, lp[s]);
+  m = wave_max(m);
+  float amax = 0.0f;
+  if (m == -__builtin_inff()) {
+    for (int e = 0; e < VPL; ++e) o[row * D + lane * VPL + e] = 0;
+    if (lane == 0 && lse) lse[row] = -__builtin_inff();
+  } else {
+    float sum = 0.0f;
+    for (int s = lane; s < nsplit; s += 64) sum += __expf(lp[s] - m);
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) sum += xor_lane(sum, msk);
+    const float L = m + __logf(sum);
+    float acc[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) acc[e] = 0.0f;
+    const float* op = o_part + row * nsplit * D + lane * VPL;
+    for (int s = 0; s < nsplit; ++s) {
+      const float w = __expf(lp[s] - L);
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) acc[e] += w * op[(long long)s * D + e];
+    }
+#pragma unroll
+    for (int e = 0; e < VPL; e += 2) {
+      const float hi = (e + 1 < VPL) ? acc[e + 1] : 0.0f;
+      const uint32_t w = pack_bf16x2(acc[e], hi);
+      if (VPL >= 2) {
+        *(uint32_t*)(o + row * D + lane * VPL + e) = w;
+      } else {
+        o[row * D + lane * VPL + e] = (uint16_t)(w & 0xFFFF);
+      }
+      amax = fmaxf(amax, fabsf(bf16_bits_to_float(w & 0xFFFF)));
+      if (e + 1 < VPL) amax = fmaxf(amax, fabsf(bf16_bits_to_float(w >> 16)));
+    }
+    if (lane == 0 && lse) lse[row] = L;
+  }
+  if (o_amax) {
+    amax = wave_max(amax);
+    if (lane == 0) atomic_max_nonneg(o_amax, amax);
+  }
+}
+
+}  // namespace fmha

@@ -1,0 +1,319 @@
+// fmha_api.cpp -- the C ABI of libfmha.so for attention (see include/fmha.h):
+// argument validation, kernel selection, workspace layout and launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fmha.h"
+#include "attn_kernels.hpp"
+#include "host_common.hpp"
+
+namespace fmha {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+fmha_status fail(fmha_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fmha_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(FMHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FMHA_OK;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Tile configuration of the decode kernel for a head dim and a row count.
+struct DecodeCfg {
+  int nw;  // waves per workgroup (16 query rows each)
+  int kt;  // keys per tile
+};
+
+DecodeCfg decode_cfg(int D, int rows_per_kv) {
+  if (D == 512) return {4, 32};
+  if (rows_per_kv <= 16) return {1, D == 64 ? 64 : 32};
+  return {4, 64};
+}
+
+bool decode_dim_ok(int D) { return D == 64 || D == 128 || D == 512; }
+bool fwd_dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+fmha_status check_common(const void* q, const void* k, const void* v, const void* o, int B,
+                         int Hq, int Hkv, int Sq, int Sk, float scale, int causal) {
+  if (!q || !k || !v || !o) return fail(FMHA_ERR_NULL, "q, k, v and o must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1)
+    return fail(FMHA_ERR_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Sk=%d)", B, Hq, Hkv,
+                Sq, Sk);
+  if (Hq % Hkv != 0) return fail(FMHA_ERR_GQA, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(FMHA_ERR_ARG, "causal must be 0 or 1");
+  if (causal && Sq > Sk)
+    return fail(FMHA_ERR_SHAPE, "causal attention needs Sq <= Sk (Sq=%d Sk=%d)", Sq, Sk);
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(FMHA_ERR_ARG, "scale must be positive and finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(FMHA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  return FMHA_OK;
+}
+
+bool sizes_fit(long long B, long long Hq, long long Hkv, long long Sq, long long Sk, long long D) {
+  // 64-bit element offsets are used throughout; keep every tensor below 2^62 bytes and the
+  // grid within HIP's limits.
+  return B * Hq * Sq * D < (1LL << 61) && B * Hkv * Sk * D < (1LL << 61) && B <= 65535 &&
+         Hkv <= 65535;
+}
+
+template <int D, int MT, int NW, int KT, bool C, bool S>
+fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, C, S>), grid, dim3(NW * 64), 0, st, p);
+  return check_launch("attention kernel launch");
+}
+
+template <int D, int MT, int NW, int KT>
+fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
+                           hipStream_t st) {
+  if (causal)
+    return split ? launch_attn<D, MT, NW, KT, true, true>(p, grid, st)
+                 : launch_attn<D, MT, NW, KT, true, false>(p, grid, st);
+  return split ? launch_attn<D, MT, NW, KT, false, true>(p, grid, st)
+               : launch_attn<D, MT, NW, KT, false, false>(p, grid, st);
+}
+
+// Prefill: 4 waves of 32 rows = 128 query rows per workgroup, 64-key tiles.
+fmha_status dispatch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_attn_cs<16, 32, 4, 64>(p, grid, causal, false, st);
+    case 32: return launch_attn_cs<32, 32, 4, 64>(p, grid, causal, false, st);
+    case 64: return launch_attn_cs<64, 32, 4, 64>(p, grid, causal, false, st);
+    case 128: return launch_attn_cs<128, 32, 4, 64>(p, grid, causal, false, st);
+  }
+  return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dim %d not built", D);
+}
+
+fmha_status dispatch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
+                            bool split, hipStream_t st) {
+  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 64>(p, grid, causal, split, st);
+  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64>(p, grid, causal, split, st);
+  if (D == 512) return launch_attn_cs<512, 16, 4, 32>(p, grid, causal, split, st);
+  return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
+}
+
+fmha_status dispatch_combine(int D, const float* op, const float* lp, uint16_t* o, float* lse,
+                             float* amax, long long nrows, int nsplit, hipStream_t st) {
+  const int rows_per_block = 4;
+  dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    case 128:
+      hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    case 512:
+      hipLaunchKernelGGL(lse_combine_kernel<512>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    default:
+      return fail(FMHA_ERR_HEAD_DIM, "combine: head dim %d not built", D);
+  }
+  return check_launch("combine kernel launch");
+}
+
+int num_cus() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return n > 0 ? n : 256;
+  }();
+  return cus;
+}
+
+// Keys per split: equal ranges rounded up to the KV tile.
+int split_len_for(int Sk, int nsplit, int kt) {
+  int len = (Sk + nsplit - 1) / nsplit;
+  return (len + kt - 1) / kt * kt;
+}
+
+}  // namespace
+
+int default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv) return 1;
+  const int rows = (Hq / Hkv) * Sq;
+  const DecodeCfg c = decode_cfg(D, rows);
+  const long long n_rb = (rows + 16 * c.nw - 1) / (16 * c.nw);
+  const long long units = (long long)B * Hkv * n_rb;
+  // Aim for about 8 resident waves per CU, keep at least 4 tiles per split.
+  const long long want_waves = 8LL * num_cus();
+  int ns = 1;
+  while ((long long)ns * units * c.nw < want_waves && ns < 1024 &&
+         Sk / (2 * ns) >= 4 * c.kt)
+    ns *= 2;
+  return ns;
+}
+
+}  // namespace fmha
+
+using namespace fmha;
+
+extern "C" {
+
+const char* fmha_status_string(fmha_status s) {
+  switch (s) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_NULL: return "null pointer";
+    case FMHA_ERR_SHAPE: return "invalid shape";
+    case FMHA_ERR_HEAD_DIM: return "unsupported head dimension";
+    case FMHA_ERR_GQA: return "Hq is not a multiple of Hkv";
+    case FMHA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FMHA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FMHA_ERR_HIP: return "HIP error";
+    case FMHA_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+const char* fmha_last_error(void) { return g_last_error; }
+
+fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                     void* stream) {
+  g_last_error[0] = 0;
+  fmha_status s = check_common(q, k, v, o, B, Hq, Hkv, Sq, Sk, scale, causal);
+  if (s != FMHA_OK) return s;
+  if (lse && !aligned16(lse)) return fail(FMHA_ERR_ALIGN, "lse must be 16-byte aligned");
+  if (!fwd_dim_ok(D)) return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd supports D in {16,32,64,128}, got %d", D);
+  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D)) return fail(FMHA_ERR_SHAPE, "tensor too large");
+  AttnParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.rows_per_kv = (Hq / Hkv) * Sq;
+  p.n_row_blocks = (p.rows_per_kv + 127) / 128;
+  p.nsplit = 1;
+  p.split_len = (Sk + 63) / 64 * 64;
+  p.scale_log2 = scale * kLog2e;
+  dim3 grid(p.n_row_blocks, Hkv, B);
+  return dispatch_fwd(D, p, grid, causal != 0, (hipStream_t)stream);
+}
+
+int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  return default_splits(B, Hq, Hkv, Sq, Sk, D);
+}
+
+size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                          int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv || !decode_dim_ok(D) ||
+      num_splits < 0 || num_splits > 1024)
+    return 0;
+  int ns = num_splits ? num_splits : default_splits(B, Hq, Hkv, Sq, Sk, D);
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * Sq;
+  return round_up(rows * ns * D * sizeof(float), kAlign) +
+         round_up(rows * ns * sizeof(float), kAlign);
+}
+
+fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                int causal, int num_splits, void* workspace,
+                                size_t workspace_bytes, float* o_amax, void* stream) {
+  g_last_error[0] = 0;
+  fmha_status s = check_common(q, k, v, o, B, Hq, Hkv, Sq, Sk, scale, causal);
+  if (s != FMHA_OK) return s;
+  if (lse && !aligned16(lse)) return fail(FMHA_ERR_ALIGN, "lse must be 16-byte aligned");
+  if (o_amax && ((uintptr_t)o_amax & 3)) return fail(FMHA_ERR_ALIGN, "o_amax must be 4-byte aligned");
+  if (!decode_dim_ok(D))
+    return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv supports D in {64,128,512}, got %d", D);
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(FMHA_ERR_ARG, "num_splits must be in 0..1024, got %d", num_splits);
+  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D)) return fail(FMHA_ERR_SHAPE, "tensor too large");
+
+  const int rows_per_kv = (Hq / Hkv) * Sq;
+  const DecodeCfg c = decode_cfg(D, rows_per_kv);
+  int ns = num_splits ? num_splits : default_splits(B, Hq, Hkv, Sq, Sk, D);
+  const int split_len = split_len_for(Sk, ns, c.kt);
+  const int ns_eff = (Sk + split_len - 1) / split_len;  // trailing empty ranges dropped
+
+  AttnParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.o_amax = o_amax;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.rows_per_kv = rows_per_kv;
+  p.n_row_blocks = (rows_per_kv + 16 * c.nw - 1) / (16 * c.nw);
+  p.nsplit = ns_eff;
+  p.split_len = split_len;
+  p.scale_log2 = scale * kLog2e;
+  const hipStream_t st = (hipStream_t)stream;
+
+  if (ns_eff <= 1) {
+    dim3 grid(p.n_row_blocks, Hkv, B);
+    return dispatch_decode(D, c, p, grid, causal != 0, false, st);
+  }
+
+  const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns);
+  if (!workspace || workspace_bytes < need)
+    return fail(FMHA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FMHA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  const size_t rows = (size_t)B * Hq * Sq;
+  p.o_part = (float*)workspace;
+  p.lse_part = (float*)((char*)workspace + round_up(rows * ns * D * sizeof(float), kAlign));
+  dim3 grid(p.n_row_blocks * ns_eff, Hkv, B);
+  s = dispatch_decode(D, c, p, grid, causal != 0, true, st);
+  if (s != FMHA_OK) return s;
+  return dispatch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, (long long)rows,
+                          ns_eff, st);
+}
+
+fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,
+                                 int D, float scale, void* stream) {
+  g_last_error[0] = 0;
+  if (!q || !k || !s_out) return fail(FMHA_ERR_NULL, "q, k and s_out must be non-null");
+  if (Sq < 1 || Sk < 1 || Sq > 128 || Sk > 128)
+    return fail(FMHA_ERR_SHAPE, "debug scores need 1 <= Sq, Sk <= 128");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(s_out))
+    return fail(FMHA_ERR_ALIGN, "q, k and s_out must be 16-byte aligned");
+  const hipStream_t st = (hipStream_t)stream;
+  switch (D) {
+    case 16: hipLaunchKernelGGL(qk_scores_debug_kernel<16>, dim3(1), dim3(256), 0, st,
+                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
+    case 32: hipLaunchKernelGGL(qk_scores_debug_kernel<32>, dim3(1), dim3(256), 0, st,
+                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
+    case 64: hipLaunchKernelGGL(qk_scores_debug_kernel<64>, dim3(1), dim3(256), 0, st,
+                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
+    case 128: hipLaunchKernelGGL(qk_scores_debug_kernel<128>, dim3(1), dim3(256), 0, st,
+                                 (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
+    default: return fail(FMHA_ERR_HEAD_DIM, "debug scores support D in {16,32,64,128}");
+  }
+  return check_launch("debug score kernel launch");
+}
+
+}  // extern "C"

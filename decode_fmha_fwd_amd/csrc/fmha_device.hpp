@@ -1,0 +1,139 @@
+// fmha_device.hpp -- gfx950 device primitives for the attention kernels:
+// MFMA tile wrappers, bf16 packing, exp2, wavefront cross-lane reductions and
+// the LDS transpose read used to feed V to the matrix cores.
+//
+// Register layouts of the two bf16 MFMA shapes used here (lane = 0..63):
+//   v_mfma_f32_32x32x16_bf16  A[32 x 16] * B[16 x 32] -> C[32 x 32]
+//     A: lane holds A[lane % 32][8*(lane / 32) + e], e = 0..7
+//     B: lane holds B[8*(lane / 32) + e][lane % 32]
+//     C: lane holds C[8*(r / 4) + 4*(lane / 32) + r % 4][lane % 32], r = 0..15
+//   v_mfma_f32_16x16x32_bf16  A[16 x 32] * B[32 x 16] -> C[16 x 16]
+//     A: lane holds A[lane % 16][8*(lane / 16) + e]
+//     B: lane holds B[8*(lane / 16) + e][lane % 16]
+//     C: lane holds C[4*(lane / 16) + r][lane % 16], r = 0..3
+// Because a contraction index may be permuted freely as long as A and B agree,
+// the kernels choose which key or head-dim element sits in each k-slot.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), per group of 16 lanes: source lane
+// 4*j + a supplies the address of four consecutive bf16 elements; destination
+// lane 4*a + e receives, for j = 0..3, element e of source lane 4*j + a.
+// Pointing source lane (j, a) at row (r0 + j), columns (c0 + 4a .. c0 + 4a + 3)
+// of a row-major tile therefore gives lane (4a + e) the column c0 + 4a + e of
+// rows r0 .. r0 + 3: a column read, which is what an MFMA operand that
+// contracts over rows needs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmha {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+#define FMHA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for "no score seen yet": exp2(x - kNegBig) never becomes
+// NaN the way (-inf) - (-inf) would for a row whose first tile is masked.
+constexpr float kNegBig = -1.0e30f;
+
+template <int MT> struct Mfma;
+
+template <> struct Mfma<32> {
+  using Acc = f32x16;
+  static constexpr int kRegs = 16;
+  static constexpr int kK = 16;          // contraction length per instruction
+  static constexpr int kKGroups = 2;     // lane groups that split the contraction
+  __device__ static inline Acc run(bf16x8 a, bf16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<16> {
+  using Acc = f32x4;
+  static constexpr int kRegs = 4;
+  static constexpr int kK = 32;
+  static constexpr int kKGroups = 4;
+  __device__ static inline Acc run(bf16x8 a, bf16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row index (within an MT-row block) of accumulator register r in this lane.
+template <int MT> __device__ inline int acc_row(int lane, int r);
+template <> __device__ inline int acc_row<32>(int lane, int r) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+template <> __device__ inline int acc_row<16>(int lane, int r) { return 4 * (lane >> 4) + r; }
+
+// Two floats -> two bf16 (round to nearest even, the hardware conversion)
+// packed low/high into one dword.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ inline float bf16_bits_to_float(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane exchange of one float with lane ^ mask (mask 16 or 32).
+__device__ inline float xor_lane(float v, int mask) {
+  int lane = __lane_id();
+  int src = lane ^ mask;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+// Reductions over the lanes that hold the same query column of an MT-wide
+// MFMA output (lanes that differ only in bits above log2(MT)).
+template <int MT> __device__ inline float group_max(float v);
+template <> __device__ inline float group_max<32>(float v) { return fmaxf(v, xor_lane(v, 32)); }
+template <> __device__ inline float group_max<16>(float v) {
+  v = fmaxf(v, xor_lane(v, 16));
+  return fmaxf(v, xor_lane(v, 32));
+}
+template <int MT> __device__ inline float group_sum(float v);
+template <> __device__ inline float group_sum<32>(float v) { return v + xor_lane(v, 32); }
+template <> __device__ inline float group_sum<16>(float v) {
+  v += xor_lane(v, 16);
+  return v + xor_lane(v, 32);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, xor_lane(v, m));
+  return v;
+}
+
+// LDS transpose read of four bf16 (see the header comment).
+__device__ inline u32x2 lds_read_tr16(const FMHA_LDS void* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FMHA_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ inline u32x4 lds_read_b128(const FMHA_LDS void* p) {
+  return *(const FMHA_LDS u32x4*)p;
+}
+
+__device__ inline void lds_write_b128(FMHA_LDS void* p, u32x4 v) { *(FMHA_LDS u32x4*)p = v; }
+
+__device__ inline u32x4 global_load_b128(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// Float bits of a non-negative float order like unsigned integers, so a
+// max over magnitudes can use an integer atomic.
+__device__ inline void atomic_max_nonneg(float* addr, float v) {
+  atomicMax((unsigned int*)addr, __builtin_bit_cast(unsigned int, v));
+}
+
+}  // namespace fmha

@@ -1,0 +1,159 @@
+/*
+ * fmha.h -- C ABI of libfmha.so: fused multi-head attention forward, split-KV
+ * decode with a log-sum-exp combine, and an NVFP4 output quantiser, as
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The page "NVFP4-1.1_RAW_CUDA_CPP_APPROACH.md" (its
+ * seven-point feature list) names the parts of the fused kernel: a QK matrix
+ * product, an in-kernel softmax with rescaling of the output accumulator, a
+ * loop over several KV tiles, a PV product, a correction epilogue and an FP4
+ * quantisation of the output; the same page names multi-CTA (split-KV) work
+ * and head dimension 512 among the goals.  Written out:
+ *
+ *     S[i, j] = scale * sum_d Q[i, d] * K[j, d]       (bf16 inputs, fp32 sum)
+ *     P[i, j] = exp(S[i, j] - LSE[i]),   LSE[i] = log sum_{j visible} exp(S[i, j])
+ *     O[i, :] = sum_{j visible} P[i, j] * V[j, :]
+ *
+ * The page "CURRENT ISSUE: UMMA QK GEMM -- 4x Scaling Bug" (section "The 4x
+ * Bug") is the reminder that S must equal the scalar dot product times
+ * `scale`, with no other factor.
+ *
+ * Conventions shared by every call:
+ *   - bf16 tensors are raw 16-bit patterns (uint16), row-major, last index
+ *     fastest, in the (batch, head, sequence, head_dim) order used for Q on the
+ *     page "nvfp4-megamoe-kernel/CURRENT_ISSUE.md" (Q viewed as (B, H, 1, HD),
+ *     batch stride H*HD):
+ *         q [B, Hq, Sq, D]   k [B, Hkv, Sk, D]   v [B, Hkv, Sk, D]
+ *         o [B, Hq, Sq, D]   lse [B, Hq, Sq] (fp32, natural log)
+ *   - Grouped heads: query head h reads KV head h / (Hq / Hkv).
+ *   - Causal mask, aligned to the bottom-right corner: key j is visible to query
+ *     row i iff j <= i + (Sk - Sq).  Masked keys are left out entirely.
+ *   - All pointers are DEVICE pointers owned by the caller and must be 16-byte
+ *     aligned; the library never allocates device memory and never
+ *     synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and runs asynchronously.
+ *   - Every argument is checked on the host before anything is launched; on
+ *     any error nothing is written and a non-zero fmha_status comes back.
+ *     After each launch the HIP launch status is checked (FMHA_ERR_HIP).
+ *   - Thread-safe: the only library state is a per-thread error string and a
+ *     cached device-property query.
+ */
+#ifndef FMHA_H
+#define FMHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FMHA_OK = 0,
+    FMHA_ERR_NULL = 1,       /* a required pointer is NULL                          */
+    FMHA_ERR_SHAPE = 2,      /* a size < 1, causal with Sq > Sk, cols % 16 != 0 ... */
+    FMHA_ERR_HEAD_DIM = 3,   /* head dimension not built for this entry point       */
+    FMHA_ERR_GQA = 4,        /* Hq is not a multiple of Hkv                         */
+    FMHA_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
+    FMHA_ERR_WORKSPACE = 6,  /* workspace missing or smaller than the size query    */
+    FMHA_ERR_HIP = 7,        /* a HIP launch or runtime call failed                 */
+    FMHA_ERR_ARG = 8         /* another argument out of range (scale <= 0 or NaN,
+                                num_splits < 0, ...)                               */
+} fmha_status;
+
+/*
+ * Fused attention forward (prefill and general Sq).
+ *   q, k, v: bf16, layouts above.  o: bf16 [B, Hq, Sq, D] output.
+ *   lse: fp32 [B, Hq, Sq] output, or NULL to skip it.
+ *   D in {16, 32, 64, 128}.  scale > 0 (e.g. 1/sqrt(D) rounded to fp32).
+ *   causal: 0 or 1 (causal requires Sq <= Sk).
+ * One workgroup computes a 128-row tile of query rows against all visible KV
+ * tiles with an online softmax (the feature list's "softmax with O rescale"
+ * over "multi-KV-tile" loops), then normalises and stores O and LSE.
+ */
+fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                     void* stream);
+
+/*
+ * Bytes of device workspace fmha_decode_splitkv needs for these sizes and this
+ * number of splits (0 = the library's choice, see fmha_decode_default_splits).
+ * Returns 0 when no workspace is needed (one split) or the sizes are invalid.
+ */
+size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                          int num_splits);
+
+/*
+ * Split-KV decode (small Sq, e.g. 1): the keys of each (batch, KV head) are cut
+ * into num_splits contiguous ranges (equal lengths rounded up to the KV tile;
+ * trailing splits may be empty).  One workgroup handles all query rows that
+ * share a KV head (the Hq/Hkv grouped heads times Sq) over one range and writes
+ * an fp32 partial output and its log-sum-exp to the workspace; a second kernel
+ * combines them:  LSE = m + log sum_s exp(lse_s - m),  m = max_s lse_s,
+ * O = sum_s exp(lse_s - LSE) * O_s.   With one split the first kernel writes
+ * O and LSE directly and no workspace is used.
+ *   D in {64, 128, 512}; Sq*Hq/Hkv <= 64 rows per KV head.
+ *   num_splits: 0 = heuristic, otherwise 1..1024.
+ *   workspace / workspace_bytes: device buffer of at least
+ *     fmha_decode_splitkv_workspace_size(...) bytes (may be NULL when that is 0).
+ *   o_amax: NULL, or a device fp32 that the call raises to max(*o_amax, max|O|)
+ *     over the bf16 O it writes (the caller initialises it, e.g. to 0); this
+ *     folds the NVFP4 quantiser's tensor-wide amax into the decode.
+ */
+fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                int causal, int num_splits, void* workspace,
+                                size_t workspace_bytes, float* o_amax, void* stream);
+
+/* The split count used when num_splits == 0. */
+int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D);
+
+/*
+ * Bytes of device workspace nvfp4_quantize needs (room for one fp32 amax).
+ */
+size_t nvfp4_quantize_workspace_size(long long rows, int cols);
+
+/*
+ * NVFP4 quantisation of a bf16 matrix x [rows, cols], cols % 16 == 0 (the
+ * feature list's last item, "FP4 quantization" of the output).  Recipe, every
+ * step one correctly rounded fp32 operation:
+ *   amax = max |x| (over the whole tensor, or *amax_in when given);
+ *   g = amax / 2688  (2688 = 6 * 448)                      -> *global_scale
+ *   per block of 16 contiguous elements of a row:
+ *     s = E4M3((amax_block / 6) / g)     (OCP E4M3FN, nearest-even, saturating)
+ *     t = value(s) * g
+ *     code = E2M1(x / t)                 (OCP E2M1, nearest-even, saturating;
+ *                                         bit 3 = sign of x / t)
+ *   codes [rows, cols/2]: byte = code[2k+1] << 4 | code[2k];
+ *   scales [rows, cols/16]: one E4M3 byte per block, row-major.
+ * amax == 0 (or g underflowing to 0) gives g = 0 and all codes and scales 0; a
+ * block with s == 0 (or t underflowing to 0) gets all codes 0.
+ *   amax_in: NULL, or a device fp32 holding max|x| (e.g. the o_amax of
+ *     fmha_decode_splitkv), which skips the amax pass.
+ *   workspace: at least nvfp4_quantize_workspace_size() bytes (used only when
+ *     amax_in is NULL).
+ */
+fmha_status nvfp4_quantize(const void* x, long long rows, int cols, uint8_t* codes,
+                           uint8_t* scales, float* global_scale, const float* amax_in,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: the raw score tile S = scale * Q K^T of the first (batch, head),
+ * for Sq, Sk <= 128 and D in {16, 32, 64, 128}, computed by the same device
+ * routine the attention kernels use for their QK product; s_out is fp32
+ * [Sq, Sk].  Lets a test check the product against the exact scalar dot
+ * product on integer-valued inputs (a 4x-class fault cannot hide).
+ */
+fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,
+                                 int D, float scale, void* stream);
+
+const char* fmha_status_string(fmha_status s);
+
+/* Detail for the calling thread's last non-OK return ("" if none). */
+const char* fmha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_H */

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         for f in ("oracle_double_to_bf16_array", "oracle_bf16_to_double_array",
                   "oracle_e4m3_encode_array", "oracle_e2m1_encode_array"):
             getattr(L, f).restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = i32
         for f in ("oracle_attention", "oracle_attention_splits", "oracle_combine",
                   "oracle_nvfp4_quantize"):
             getattr(L, f).restype = i32
@@ -190,6 +192,11 @@ def nvfp4_quantize(x_bits, rows, cols):
     if rc:
         raise ValueError(f"oracle_nvfp4_quantize failed with code {rc}")
     return codes, scales, g[0]
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().oracle_num_threads()
 
 
 def e4m3_value(c: int) -> float:

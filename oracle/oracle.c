@@ -386,3 +386,13 @@ void oracle_e2m1_encode_array(const float *x, long long n, uint8_t *out)
 {
     for (long long i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(x[i]);
 }
+
+/* Threads the OpenMP loops above will use (for reporting). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched): the
+library loads, exports every function include/fmha.h declares, and rejects bad
+arguments with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_fmha_fwd_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fmha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = F.load_library()
+    names = declared_functions()
+    assert {"fmha_fwd", "fmha_decode_splitkv", "nvfp4_quantize"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(F.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    lib = F.load_library()
+    for s in range(9):
+        assert lib.fmha_status_string(s)
+    assert lib.fmha_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every case below fails validation first
+
+
+def call_fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=64,
+             scale=0.125, causal=0):
+    return F.load_library().fmha_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, None)
+
+
+def call_dec(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=1, Sq=1, Sk=1024, D=64,
+             scale=0.125, causal=0, ns=4, ws=None, wsb=0, amax=None):
+    return F.load_library().fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale,
+                                                causal, ns, ws, wsb, amax, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(Sk=0), 2), (dict(Sq=5, Sk=4, causal=1), 2),
+    (dict(D=48), 3), (dict(D=512), 3),
+    (dict(Hq=3, Hkv=2), 4),
+    (dict(q=FAKE + 8), 5), (dict(lse=FAKE + 4), 5),
+    (dict(scale=0.0), 8), (dict(scale=float("nan")), 8), (dict(causal=2), 8),
+])
+def test_fwd_validation(kw, status):
+    assert call_fwd(**kw) == status
+    assert F.load_library().fmha_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(Hq=6, Hkv=4), 4), (dict(D=16), 3), (dict(D=256), 3),
+    (dict(ns=-1), 8), (dict(ns=2000), 8), (dict(v=FAKE + 2), 5),
+    (dict(ns=4, ws=None, wsb=0), 6), (dict(ns=4, ws=FAKE, wsb=16), 6),
+    (dict(ns=4, ws=FAKE + 8, wsb=1 << 30), 5), (dict(amax=FAKE + 1), 5),
+])
+def test_decode_validation(kw, status):
+    assert call_dec(**kw) == status
+
+
+def test_workspace_formula():
+    # rows * splits * (D + 1) floats, each section rounded up to 256 bytes
+    rows, ns, D = 64 * 32, 16, 64
+    want = -(-rows * ns * D * 4 // 256) * 256 + -(-rows * ns * 4 // 256) * 256
+    assert F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 64, 16) == want
+    assert F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 64, 1) == 0
+    assert F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 48, 4) == 0
+    assert F.fmha_decode_splitkv_workspace_size(64, 32, 7, 1, 8192, 64, 4) == 0
+
+
+def test_default_splits_heuristic():
+    ns = F.fmha_decode_default_splits
+    for args in [(64, 32, 8, 1, 8192, 64), (32, 64, 1, 1, 16384, 512), (128, 16, 16, 1, 4096, 128),
+                 (1, 1, 1, 1, 100, 64)]:
+        n = ns(*args)
+        assert 1 <= n <= 1024 and (n & (n - 1)) == 0
+    assert ns(1, 1, 1, 1, 100, 64) == 1            # too short to split
+    assert ns(32, 64, 1, 1, 16384, 512) >= 8       # 32 (batch, KV head) units need splitting
+
+
+def test_nvfp4_validation():
+    lib = F.load_library()
+    q = lib.nvfp4_quantize
+    assert q(None, 4, 16, FAKE, FAKE, FAKE, None, FAKE, 256, None) == 1
+    assert q(FAKE, 4, 24, FAKE, FAKE, FAKE, None, FAKE, 256, None) == 2
+    assert q(FAKE, 0, 16, FAKE, FAKE, FAKE, None, FAKE, 256, None) == 2
+    assert q(FAKE + 2, 4, 16, FAKE, FAKE, FAKE, None, FAKE, 256, None) == 5
+    assert q(FAKE, 4, 16, FAKE, FAKE, FAKE, None, None, 0, None) == 6
+    assert lib.nvfp4_quantize_workspace_size(4, 16) >= 4
+
+
+def test_debug_scores_validation():
+    lib = F.load_library()
+    assert lib.fmha_debug_qk_scores(FAKE, FAKE, FAKE, 129, 4, 64, 1.0, None) == 2
+    assert lib.fmha_debug_qk_scores(FAKE, FAKE, FAKE, 4, 4, 512, 1.0, None) == 3
+    assert lib.fmha_debug_qk_scores(None, FAKE, FAKE, 4, 4, 64, 1.0, None) == 1

@@ -1,0 +1,173 @@
+"""GPU parity of the attention kernels (prefill fmha_fwd and split-KV decode
+fmha_decode_splitkv) against the fp64 CPU oracle, through the C ABI.
+
+Small shapes are compared element by element on every row; the full-size
+workloads are compared on a seeded sample of rows (the oracle evaluates them
+one by one), in the same launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import decode_fmha_fwd_amd as F
+from gpu_helpers import assert_parity, bits, oracle_rows, poison_like, require_gpu
+from workloads import WORKLOADS, default_scale, make_qkv, make_workload_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, scale, causal):
+    dev = require_gpu()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    o = poison_like(qd)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    F.fmha_fwd(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_decode(q, k, v, scale, causal, num_splits, o_amax=None):
+    dev = require_gpu()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    o = poison_like(qd)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    nb = F.fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, num_splits)
+    ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=dev)
+    F.fmha_decode_splitkv(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+                          ws, nb, o_amax)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------- QK exactness
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("Sq,Sk", [(128, 128), (77, 101)])
+def test_qk_scores_equal_exact_dot_product(D, Sq, Sk):
+    """Integer inputs in [-8, 8]: every partial sum is an integer < 2^24, so the
+    MFMA product must equal scale * <q, k> exactly -- a stray factor (the 4x
+    chased on the QK page) or a misplaced operand cannot pass."""
+    dev = require_gpu()
+    rng = np.random.default_rng(D + Sq)
+    qi = rng.integers(-8, 9, size=(Sq, D))
+    ki = rng.integers(-8, 9, size=(Sk, D))
+    q = torch.tensor(qi, dtype=torch.bfloat16, device=dev)
+    k = torch.tensor(ki, dtype=torch.bfloat16, device=dev)
+    for scale in (0.25, 0.125):
+        s = torch.full((Sq, Sk), float("nan"), dtype=torch.float32, device=dev)
+        F.fmha_debug_qk_scores(q, k, s, Sq, Sk, D, scale)
+        torch.cuda.synchronize()
+        expect = scale * (qi @ ki.T).astype(np.float64)
+        np.testing.assert_array_equal(s.cpu().numpy().astype(np.float64), expect)
+
+
+# ---------------------------------------------------------------- prefill
+
+def test_single_tile_d16_workload():
+    w = WORKLOADS["single_tile_d16"]
+    q, k, v = make_workload_inputs(w)
+    o, lse = run_fwd(q, k, v, w.scale, w.causal)
+    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=w.name)
+
+
+FWD_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal
+    (1, 1, 1, 128, 128, 16, True),
+    (2, 2, 2, 200, 200, 64, False),     # ragged: 200 = 3 x 64 + 8
+    (2, 2, 2, 200, 200, 64, True),
+    (1, 4, 2, 130, 333, 64, True),      # GQA, Sq < Sk (bottom-right causal)
+    (1, 2, 1, 1, 77, 64, False),        # a single query row
+    (1, 2, 2, 257, 257, 32, True),
+    (1, 2, 2, 190, 300, 128, False),
+    (1, 1, 1, 64, 1, 64, False),        # one key
+    (3, 3, 1, 45, 45, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES)
+def test_fwd_small_shapes(case):
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=sum(case))
+    scale = default_scale(D)
+    o, lse = run_fwd(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle_rows(q, k, v, scale, causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=str(case))
+
+
+def test_prefill_causal_d64_workload_sampled():
+    w = WORKLOADS["prefill_causal_d64"]
+    q, k, v = make_workload_inputs(w)
+    o, lse = run_fwd(q, k, v, w.scale, w.causal)
+    rows = sample_rows(w.B * w.Hq * w.Sq, 768, seed=7)
+    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=w.name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_fwd_is_deterministic():
+    q, k, v = make_qkv(1, 2, 2, 300, 300, 64, seed=3)
+    o1, l1 = run_fwd(q, k, v, 0.125, True)
+    o2, l2 = run_fwd(q, k, v, 0.125, True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- decode
+
+DEC_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, num_splits
+    (2, 8, 2, 1, 1000, 64, False, 1),
+    (2, 8, 2, 1, 1000, 64, False, 3),
+    (2, 8, 2, 1, 1000, 64, False, 16),
+    (2, 8, 2, 1, 1000, 64, False, 0),
+    (1, 64, 1, 1, 777, 512, False, 4),
+    (1, 64, 1, 1, 300, 512, False, 1),
+    (3, 4, 4, 1, 513, 128, False, 1),
+    (3, 4, 4, 1, 513, 128, False, 5),
+    (2, 16, 2, 4, 390, 64, True, 2),    # small Sq > 1, causal bottom-right
+    (2, 32, 1, 2, 129, 128, False, 2),  # 64 rows per KV head, 4 waves
+    (1, 4, 1, 1, 1, 64, False, 1),      # one key
+    (1, 2, 1, 1, 40, 64, False, 8),     # more splits than tiles: empty ranges
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES)
+def test_decode_small_shapes(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, ns = case
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=sum(case), sigma=0.7)
+    scale = default_scale(D)
+    o, lse = run_decode(q, k, v, scale, causal, ns)
+    o_ref, lse_ref = oracle_rows(q, k, v, scale, causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=str(case))
+
+
+@pytest.mark.parametrize("name", ["decode_gqa_d64", "decode_mqa_d512", "decode_nvfp4_d128"])
+def test_decode_workloads_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v = make_workload_inputs(w)
+    o, lse = run_decode(q, k, v, w.scale, w.causal, w.num_splits)
+    rows = sample_rows(w.B * w.Hq * w.Sq, 96, seed=11)
+    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_split_count_does_not_change_the_result():
+    q, k, v = make_qkv(4, 8, 2, 1, 4096, 64, seed=5)
+    outs = [run_decode(q, k, v, 0.125, False, ns) for ns in (1, 2, 7, 16)]
+    base_o = outs[0][0].float()
+    for o, lse in outs[1:]:
+        assert (o.float() - base_o).abs().max().item() <= 1.6e-2
+        assert (lse - outs[0][1]).abs().max().item() <= 1e-5
+
+
+def test_decode_amax_fold():
+    dev = require_gpu()
+    q, k, v = make_qkv(4, 16, 16, 1, 512, 128, seed=9)
+    for ns in (1, 4):
+        amax = torch.zeros(1, dtype=torch.float32, device=dev)
+        o, _ = run_decode(q, k, v, default_scale(128), False, ns, o_amax=amax)
+        assert amax.item() == o.float().abs().max().item()
