@@ -14,9 +14,10 @@
 //     (MT = 32 or 16 rows per wave).  Rows are the flattened (grouped head,
 //     position) pairs of that KV head, so GQA decode packs all Hq/Hkv heads of
 //     a KV head into one workgroup and each K/V byte is read once.
-//   * K and V tiles of KT keys are loaded with 16-byte coalesced global loads
-//     into registers, written to a double-buffered LDS tile whose 16-byte
-//     chunks are XOR-swizzled by row, and read back as MFMA operands.
+//   * K and V tiles of KT keys stream from HBM straight into a ring of STAGES
+//     LDS tiles with asynchronous global->LDS copies (no registers, issued
+//     STAGES-1 tiles ahead, one barrier per tile); 16-byte chunks are
+//     XOR-swizzled by row so MFMA operand reads are free of bank conflicts.
 //   * Scores are computed transposed, S^T = K * Q^T (K is the A operand, Q^T
 //     the B operand held in registers), so each lane owns ONE query row and a
 //     set of keys: row max and row sum are in-lane plus one or two lane swaps.
@@ -112,24 +113,77 @@ __device__ inline void qk_scores(const uint16_t* ks,
   }
 }
 
-template <int D, int MT, int NW, int KT, bool CAUSAL, bool SPLIT>
+// Copies one K or V tile (KT rows of D bf16, rows clamped to the last key for
+// a ragged tail) into a swizzled LDS tile with asynchronous global->LDS
+// copies.  Each wave issues kLoads copies of 64 lanes x BYTES; copy j of wave
+// w fills the contiguous LDS slots [(j*NW + w)*64, +64) and every lane fetches
+// the global bytes that belong in its slot, so 8 lanes read one 128-byte row
+// segment and the swizzle costs nothing on the HBM side.
+template <int D, int NW, int KT>
+struct TileCopy {
+  static constexpr int kTileBytes = KT * D * 2;
+  static constexpr int kBytes = (kTileBytes >= NW * 64 * 16) ? 16 : 4;
+  static constexpr int kLoads = kTileBytes / (NW * 64 * kBytes);
+  static_assert(kLoads >= 1 && kLoads * NW * 64 * kBytes == kTileBytes,
+                "tile must split evenly over the workgroup's copies");
+
+  __device__ static inline void issue(const uint16_t* base, int t0, int Sk, FMHA_LDS char* lds,
+                                      int wave, int lane) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int slot = (j * NW + wave) * 64 + lane;
+      const int byte = slot * kBytes;
+      const int row = byte / (D * 2);
+      const int inrow = byte - row * (D * 2);
+      const int pchunk = inrow >> 4;
+      const int lchunk = pchunk ^ swz<CPR>(row);
+      const long long key = min(t0 + row, Sk - 1);
+      const uint16_t* g = base + key * D + lchunk * 8 + ((inrow & 15) >> 1);
+      dma_to_lds<kBytes>(g, (FMHA_LDS void*)(lds + (j * NW + wave) * 64 * kBytes));
+    }
+  }
+};
+
+// Waits until at most `pending` tiles (each kPerTile copies) of this wave's
+// copies are still in flight.
+template <int kPerTile, int kMaxPending>
+__device__ inline void wait_tiles(int pending) {
+  if constexpr (kMaxPending >= 2) {
+    if (pending >= 2) { wait_vmcnt<2 * kPerTile>(); return; }
+  }
+  if constexpr (kMaxPending >= 1) {
+    if (pending >= 1) { wait_vmcnt<kPerTile>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Lazy rescaling threshold (log2 units): the running maximum only moves when
+// a tile's maximum exceeds it by more than this, so most tiles skip the O
+// rescale; probabilities then stay below 2^kRescaleSlack, harmless in fp32
+// and bf16.  The final O / l and LSE are exact whichever maximum is used.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int MT, int NW, int KT, int STAGES, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
-  constexpr int NT = NW * 64;
-  constexpr int CPR = D / 8;                       // 16-byte chunks per K/V row
-  constexpr int TILE_CHUNKS = KT * CPR;
-  constexpr int NCH = (TILE_CHUNKS + NT - 1) / NT; // chunks per thread per tensor
+  using Copy = TileCopy<D, NW, KT>;
   constexpr int KSTEPS = (D + M::kK - 1) / M::kK;  // QK contraction steps
   constexpr int KBLK = KT / MT;                    // MT-key blocks per tile
   constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
   constexpr int ROWS_WG = NW * MT;
   constexpr int NPV = (MT == 32) ? 2 * KBLK : KBLK / 2;  // PV instructions per d-block
+  constexpr int TILE_ELEMS = KT * D;
+  constexpr int kPerTile = 2 * Copy::kLoads;       // copies per wave per tile (K and V)
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT % 32 == 0, "16-row waves consume 32 keys per PV step");
-  static_assert(D % 16 == 0 && CPR >= 2, "head dim must be a multiple of 16");
+  static_assert(D % 16 == 0 && D >= 16, "head dim must be a multiple of 16");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
+  static_assert(kPerTile * (STAGES - 2) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][KT * D];
+  // [stage][K | V][KT * D]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES][2][TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int diag = p.Sk - p.Sq;  // causal: key j visible to row i iff j <= i + diag
 
   // Key range of this workgroup.
-  int kbeg = split * p.split_len;
+  const int kbeg = split * p.split_len;
   int kend = min(p.Sk, kbeg + p.split_len);
   int wave_min_last = INT_MAX;  // smallest last-visible key over the wave's rows
   int wave_max_last = INT_MAX;  // largest
@@ -174,6 +228,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     }
   }
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
+  const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
+
+  auto issue_tile = [&](int it) {
+    FMHA_LDS char* st = (FMHA_LDS char*)&smem[it % STAGES][0][0];
+    Copy::issue(kbase, kbeg + it * KT, p.Sk, st, wave, lane);
+    Copy::issue(vbase, kbeg + it * KT, p.Sk, st + TILE_ELEMS * 2, wave, lane);
+  };
+
+  // Prologue: the first STAGES-1 tiles in flight before Q is even loaded.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ntiles) issue_tile(s);
 
   bf16x8 qf[KSTEPS];
   load_q_frags<D, MT>(p.q + (row_base + my_rc) * D, kg, qf);
@@ -184,136 +250,104 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   float m_run = kNegBig;
   float l_run = 0.0f;
 
-  u32x4 kreg[NCH], vreg[NCH];
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = tid + c * NT;
-      if (TILE_CHUNKS % NT == 0 || idx < TILE_CHUNKS) {
-        const int row = idx / CPR;
-        const int ch = idx - row * CPR;
-        const long long key = min(t0 + row, p.Sk - 1);  // ragged tail: clamp, masked later
-        kreg[c] = *(const u32x4*)(kbase + key * D + ch * 8);
-        vreg[c] = *(const u32x4*)(vbase + key * D + ch * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = tid + c * NT;
-      if (TILE_CHUNKS % NT == 0 || idx < TILE_CHUNKS) {
-        const int row = idx / CPR;
-        const int ch = idx - row * CPR;
-        const int off = row * D + ((ch ^ swz<CPR>(row)) << 3);
-        lds_write_b128((FMHA_LDS void*)&smem[buf][0][off], kreg[c]);
-        lds_write_b128((FMHA_LDS void*)&smem[buf][1][off], vreg[c]);
-      }
-    }
-  };
-
-  const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
-  if (ntiles > 0) {
-    load_tile(kbeg);
-    store_tile(0);
-  }
-  __syncthreads();
-
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = kbeg + it * KT;
-    const int buf = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(t0 + KT);
+    // This wave's copies of tile `it` have landed (later tiles may still fly),
+    // every wave is past its reads of tile it-1, and then everyone's copies of
+    // tile `it` are visible.
+    wait_tiles<kPerTile, STAGES - 2>(min(STAGES - 2, ntiles - 1 - it));
+    wait_lgkmcnt0();
+    lds_barrier();
+    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1);
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
-    const bool wave_active = !CAUSAL || t0 <= wave_max_last;
-    if (wave_active) {
-      const uint16_t* ks = &smem[buf][0][0];
-      const uint16_t* vs = &smem[buf][1][0];
+    if (CAUSAL && t0 > wave_max_last) continue;
 
-      // ---- S^T = K Q^T ----
-      Acc sacc[KBLK];
-      qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
+    const uint16_t* ks = &smem[it % STAGES][0][0];
+    const uint16_t* vs = &smem[it % STAGES][1][0];
 
-      // ---- mask the ragged end and the causal diagonal ----
-      const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb)
-#pragma unroll
-          for (int r = 0; r < M::kRegs; ++r) {
-            const int key = t0 + kb * MT + acc_row<MT>(lane, r);
-            if (key >= kend || key > my_last) sacc[kb][r] = -__builtin_inff();
-          }
-      }
+    // ---- S^T = K Q^T ----
+    Acc sacc[KBLK];
+    qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
 
-      // ---- online softmax (base 2) ----
-      float mloc = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < KBLK; ++kb)
-#pragma unroll
-        for (int r = 0; r < M::kRegs; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
-      mloc = group_max<MT>(mloc);
-      const float m_new = fmaxf(m_run, mloc * p.scale_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.0f;
+    // ---- mask the ragged end and the causal diagonal ----
+    const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb)
 #pragma unroll
         for (int r = 0; r < M::kRegs; ++r) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_new));
-          sacc[kb][r] = pv;
-          psum += pv;
+          const int key = t0 + kb * MT + acc_row<MT>(lane, r);
+          if (key >= kend || key > my_last) sacc[kb][r] = -__builtin_inff();
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
-
-      // ---- O^T += V^T P^T ----
-      // Source-lane coordinates for the transpose read.
-      const int grp = lane >> 4;
-      const int tj = (lane >> 2) & 3;
-      const int ta = lane & 3;
-#pragma unroll
-      for (int step = 0; step < NPV; ++step) {
-        // Probabilities as the B operand: k-slot e of lane group g.
-        u32x4 pw;
-        int row1, row2;
-        if constexpr (MT == 32) {
-          const int kb = step >> 1, t2 = step & 1;
-          pw[0] = pack_bf16x2(sacc[kb][8 * t2 + 0], sacc[kb][8 * t2 + 1]);
-          pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
-          pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
-          pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
-          // k-slots 0..3 <-> keys kofs + 4h + 0..3, slots 4..7 <-> kofs + 8 + 4h + 0..3
-          row1 = kb * 32 + 16 * t2 + 4 * (grp >> 1) + tj;
-          row2 = row1 + 8;
-        } else {
-          const int kb0 = 2 * step, kb1 = 2 * step + 1;
-          pw[0] = pack_bf16x2(sacc[kb0][0], sacc[kb0][1]);
-          pw[1] = pack_bf16x2(sacc[kb0][2], sacc[kb0][3]);
-          pw[2] = pack_bf16x2(sacc[kb1][0], sacc[kb1][1]);
-          pw[3] = pack_bf16x2(sacc[kb1][2], sacc[kb1][3]);
-          // k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
-          row1 = 32 * step + 4 * grp + tj;
-          row2 = row1 + 16;
-        }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
-          if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
-          const u32x2 lo = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row1, col)]);
-          const u32x2 hi = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row2, col)]);
-          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = M::run(__builtin_bit_cast(bf16x8, va), pb, oacc[db]);
-        }
-      }
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    // ---- online softmax (base 2) with lazy rescaling ----
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+      for (int r = 0; r < M::kRegs; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+    mloc = group_max<MT>(mloc) * p.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+      for (int r = 0; r < M::kRegs; ++r) {
+        const float pv = fast_exp2(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_run));
+        sacc[kb][r] = pv;
+        psum += pv;
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T ----
+    // Source-lane coordinates for the transpose read.
+    const int grp = lane >> 4;
+    const int tj = (lane >> 2) & 3;
+    const int ta = lane & 3;
+#pragma unroll
+    for (int step = 0; step < NPV; ++step) {
+      // Probabilities as the B operand: k-slot e of lane group g.
+      u32x4 pw;
+      int row1, row2;
+      if constexpr (MT == 32) {
+        const int kb = step >> 1, t2 = step & 1;
+        pw[0] = pack_bf16x2(sacc[kb][8 * t2 + 0], sacc[kb][8 * t2 + 1]);
+        pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
+        pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
+        pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
+        // k-slots 0..3 <-> keys kofs + 4h + 0..3, slots 4..7 <-> kofs + 8 + 4h + 0..3
+        row1 = kb * 32 + 16 * t2 + 4 * (grp >> 1) + tj;
+        row2 = row1 + 8;
+      } else {
+        const int kb0 = 2 * step, kb1 = 2 * step + 1;
+        pw[0] = pack_bf16x2(sacc[kb0][0], sacc[kb0][1]);
+        pw[1] = pack_bf16x2(sacc[kb0][2], sacc[kb0][3]);
+        pw[2] = pack_bf16x2(sacc[kb1][0], sacc[kb1][1]);
+        pw[3] = pack_bf16x2(sacc[kb1][2], sacc[kb1][3]);
+        // k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
+        row1 = 32 * step + 4 * grp + tj;
+        row2 = row1 + 16;
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
+        if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
+        const u32x2 lo = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row1, col)]);
+        const u32x2 hi = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row2, col)]);
+        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = M::run(__builtin_bit_cast(bf16x8, va), pb, oacc[db]);
+      }
+    }
   }
 
   // ---- epilogue: O / l, log-sum-exp ----

@@ -42,9 +42,12 @@ struct DecodeCfg {
   int kt;  // keys per tile
 };
 
+// One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
+// small workgroups keep enough loads in flight per CU); four waves otherwise.
+// Head dim 512 always uses four waves sharing a 32-key, 2-stage ring (128 KB).
 DecodeCfg decode_cfg(int D, int rows_per_kv) {
   if (D == 512) return {4, 32};
-  if (rows_per_kv <= 16) return {1, D == 64 ? 64 : 32};
+  if (rows_per_kv <= 16) return {1, 32};
   return {4, 64};
 }
 
@@ -75,40 +78,41 @@ bool sizes_fit(long long B, long long Hq, long long Hkv, long long Sq, long long
          Hkv <= 65535;
 }
 
-template <int D, int MT, int NW, int KT, bool C, bool S>
+template <int D, int MT, int NW, int KT, int ST, bool C, bool S>
 fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, C, S>), grid, dim3(NW * 64), 0, st, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, ST, C, S>), grid, dim3(NW * 64), 0, st, p);
   return check_launch("attention kernel launch");
 }
 
-template <int D, int MT, int NW, int KT>
+template <int D, int MT, int NW, int KT, int ST>
 fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
                            hipStream_t st) {
   if (causal)
-    return split ? launch_attn<D, MT, NW, KT, true, true>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, true, false>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, false, true>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, false, false>(p, grid, st);
+    return split ? launch_attn<D, MT, NW, KT, ST, true, true>(p, grid, st)
+                 : launch_attn<D, MT, NW, KT, ST, true, false>(p, grid, st);
+  return split ? launch_attn<D, MT, NW, KT, ST, false, true>(p, grid, st)
+               : launch_attn<D, MT, NW, KT, ST, false, false>(p, grid, st);
 }
 
-// Prefill: 4 waves of 32 rows = 128 query rows per workgroup, 64-key tiles.
+// Prefill: 4 waves of 32 rows = 128 query rows per workgroup, 64-key tiles in
+// a 3-stage LDS ring (2 stages at head dim 128).
 fmha_status dispatch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
   switch (D) {
-    case 16: return launch_attn_cs<16, 32, 4, 64>(p, grid, causal, false, st);
-    case 32: return launch_attn_cs<32, 32, 4, 64>(p, grid, causal, false, st);
-    case 64: return launch_attn_cs<64, 32, 4, 64>(p, grid, causal, false, st);
-    case 128: return launch_attn_cs<128, 32, 4, 64>(p, grid, causal, false, st);
+    case 16: return launch_attn_cs<16, 32, 4, 64, 3>(p, grid, causal, false, st);
+    case 32: return launch_attn_cs<32, 32, 4, 64, 3>(p, grid, causal, false, st);
+    case 64: return launch_attn_cs<64, 32, 4, 64, 3>(p, grid, causal, false, st);
+    case 128: return launch_attn_cs<128, 32, 4, 64, 2>(p, grid, causal, false, st);
   }
   return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dim %d not built", D);
 }
 
 fmha_status dispatch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                             bool split, hipStream_t st) {
-  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 64>(p, grid, causal, split, st);
-  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64>(p, grid, causal, split, st);
-  if (D == 512) return launch_attn_cs<512, 16, 4, 32>(p, grid, causal, split, st);
+  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 32, 3>(p, grid, causal, split, st);
+  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64, 2>(p, grid, causal, split, st);
+  if (D == 512) return launch_attn_cs<512, 16, 4, 32, 2>(p, grid, causal, split, st);
   return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
 }
 

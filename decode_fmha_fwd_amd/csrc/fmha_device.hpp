@@ -130,6 +130,46 @@ __device__ inline u32x4 global_load_b128(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
+// Asynchronous global -> LDS copy of 16 (or 4) bytes per lane
+// (global_load_lds_dwordx4 / _dword): lane l's bytes land at lds_base +
+// BYTES*l, where lds_base is the same for every lane of the wave (it goes
+// to M0).  Completion is tracked by vmcnt like any global load; the compiler
+// does not order LDS reads after these writes, so callers wait explicitly
+// (wait_vmcnt) and then barrier before reading what other waves copied.
+template <int BYTES>
+__device__ inline void dma_to_lds(const void* g, FMHA_LDS void* lds_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword copies");
+  const __attribute__((address_space(1))) void* gp = (const __attribute__((address_space(1))) void*)g;
+  if constexpr (BYTES == 16) {
+    __builtin_amdgcn_global_load_lds(gp, lds_base, 16, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds(gp, lds_base, 4, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima, i.e. not waited for).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(0): all of this wave's LDS reads and writes have finished.
+__device__ inline void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Workgroup barrier that orders LDS accesses in the compiler without the
+// memory-model fences of __syncthreads (whose release fence would also wait
+// for every outstanding LDS copy, defeating the prefetch).  Callers wait for
+// their own outstanding LDS traffic first.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Float bits of a non-negative float order like unsigned integers, so a
 // max over magnitudes can use an integer atomic.
 __device__ inline void atomic_max_nonneg(float* addr, float v) {
