@@ -6,7 +6,8 @@ compiles every ``csrc/*.hip`` with hipcc for ``--offload-arch=gfx950`` and links
 them into ``decode_fmha_fwd_amd/libfmha.so``.  Packed-fp32 instructions are
 turned off for all device code; the NVFP4 translation unit additionally keeps
 fp contraction off, correctly rounded fp32 division and fp32 denormals,
-because it decides integer codes.
+because it decides integer codes; the prefill kernels keep MFMA accumulators
+in ordinary VGPRs.
 """
 from __future__ import annotations
 
@@ -26,10 +27,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 PER_FILE = {
+    # prefill keeps MFMA accumulators in ordinary VGPRs (no AGPR round trips
+    # around the softmax); decode at head dim 512 needs the AGPR file for O
+    "fmha_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "nvfp4.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                   "-fno-gpu-flush-denormals-to-zero"],
 }
-SOURCES = ["fmha_api.hip", "nvfp4.hip"]
+SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "nvfp4.hip"]
 
 
 def hipcc() -> str:

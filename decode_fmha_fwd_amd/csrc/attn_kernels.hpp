@@ -31,40 +31,43 @@
 #pragma once
 
 #include <climits>
+#include <type_traits>
+#include <utility>
 
 #include "fmha_device.hpp"
+#include "launch.hpp"
 
 namespace fmha {
 
-struct AttnParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;          // bf16 output (no split)
-  float* lse;           // fp32 [rows] or null (no split)
-  float* o_part;        // fp32 [rows][nsplit][D] (split)
-  float* lse_part;      // fp32 [rows][nsplit]   (split)
-  float* o_amax;        // optional running max |O| (no split)
-  int Hkv;
-  int Sq;
-  int Sk;
-  int rows_per_kv;      // (Hq / Hkv) * Sq query rows share one KV head
-  int n_row_blocks;     // ceil(rows_per_kv / (NW * MT))
-  int nsplit;           // key ranges per (batch, KV head)
-  int split_len;        // keys per range, a multiple of KT
-  float scale_log2;     // scale * log2(e)
+
+// log2(min(CPR, 16)): chunk-index bits the swizzle permutes.
+template <int CPR>
+struct CPR_LOG2 {
+  static constexpr int value = CPR >= 16 ? 4 : (CPR == 8 ? 3 : (CPR == 4 ? 2 : 1));
 };
 
-// XOR swizzle of the 16-byte chunk index within a K/V row so that the 16
-// lanes of one LDS read phase, which read the same logical chunk of 16
-// consecutive rows, hit 16 distinct 16-byte bank groups.
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// XOR swizzle of the 16-byte chunk index within a K/V row.  With 64 LDS
+// banks of 4 bytes, a 16-byte read is served 16 lanes at a time and an 8-byte
+// read 32 lanes at a time.  The K operand reads (16 lanes: one chunk of 16
+// consecutive rows) and the V transpose reads (32 lanes: 4 or 8 consecutive
+// rows, a 32- or 64-byte column band) both hit distinct banks when the chunk
+// index is XORed with the bit-reversed low row bits: rows that share a bank
+// window (256 bytes = 256/(2D) rows) are spread by the reversal's high bits,
+// and neighbouring rows of a transpose read by its low bits.
 template <int CPR>
 __device__ inline int swz(int row) {
-  if constexpr (CPR >= 16) {
-    return row & 15;
-  } else {
-    return (row / (16 / CPR)) & (CPR - 1);
-  }
+  constexpr int K = CPR_LOG2<CPR>::value;
+  const unsigned x = (unsigned)(row >> (4 - K)) & ((1u << K) - 1u);
+  return (int)(__builtin_bitreverse32(x) >> (32 - K));
 }
 
 // Element offset of (row, col) in a swizzled [rows][D] bf16 tile.
@@ -100,17 +103,23 @@ __device__ inline void qk_scores(const uint16_t* ks,
   using M = Mfma<MT>;
   constexpr int KSTEPS = (D + M::kK - 1) / M::kK;
   const int kg = lane / MT;
+  u32x4 kf[KBLK][KSTEPS];
 #pragma unroll
   for (int kb = 0; kb < KBLK; ++kb) {
-    sacc[kb] = typename M::Acc{};
     const int krow = kb * MT + lane % MT;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int col = s * M::kK + 8 * kg;
-      u32x4 raw = lds_read_b128((const FMHA_LDS void*)&ks[tile_off<D>(krow, col < D ? col : 0)]);
-      sacc[kb] = M::run(__builtin_bit_cast(bf16x8, raw), qf[s], sacc[kb]);
+      kf[kb][s] = lds_read_b128((const FMHA_LDS void*)&ks[tile_off<D>(krow, col < D ? col : 0)]);
     }
   }
+#pragma unroll
+  for (int kb = 0; kb < KBLK; ++kb) sacc[kb] = typename M::Acc{};
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+      sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[kb][s]), qf[s], sacc[kb]);
 }
 
 // Copies one K or V tile (KT rows of D bf16, rows clamped to the last key for
@@ -182,18 +191,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
   static_assert(kPerTile * (STAGES - 2) < 64, "vmcnt range");
 
-  // [stage][K | V][KT * D]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGES][2][TILE_ELEMS];
+  // [K | V][stage][KT * D]: V tiles first in LDS so that every V transpose
+  // read can carry its full LDS offset as an instruction immediate (< 64 KiB).
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][STAGES][TILE_ELEMS];
+  constexpr int kV = 0, kK = 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  const int split = blockIdx.x / p.n_row_blocks;
-  int rb = blockIdx.x - split * p.n_row_blocks;
-  if (CAUSAL) rb = p.n_row_blocks - 1 - rb;  // longest key ranges start first
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1-D grid, row block slowest: with a causal mask the longest row blocks of
+  // every head are dispatched first, and since the (batch, KV head, split)
+  // count is a multiple of 8 in the usual shapes, all row blocks of one head
+  // land on the same XCD (blocks go round-robin over the 8 XCDs) and share its
+  // L2 for their K/V re-reads.
+  const int n_units = p.nsplit * p.Hkv * p.B;
+  const int rb_rank = blockIdx.x / n_units;
+  const int unit = blockIdx.x - rb_rank * n_units;
+  const int rb = CAUSAL ? p.n_row_blocks - 1 - rb_rank : rb_rank;
+  const int split = unit % p.nsplit;
+  const int bk = unit / p.nsplit;
+  const int kvh = bk % p.Hkv;
+  const int b = bk / p.Hkv;
 
   const long long bh_kv = (long long)b * p.Hkv + kvh;
   const uint16_t* __restrict__ kbase = p.k + bh_kv * p.Sk * D;
@@ -230,16 +249,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
 
-  auto issue_tile = [&](int it) {
-    FMHA_LDS char* st = (FMHA_LDS char*)&smem[it % STAGES][0][0];
-    Copy::issue(kbase, kbeg + it * KT, p.Sk, st, wave, lane);
-    Copy::issue(vbase, kbeg + it * KT, p.Sk, st + TILE_ELEMS * 2, wave, lane);
+  auto issue_tile = [&](int it, int stage) {
+    Copy::issue(kbase, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&smem[kK][stage][0], wave, lane);
+    Copy::issue(vbase, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&smem[kV][stage][0], wave, lane);
   };
 
   // Prologue: the first STAGES-1 tiles in flight before Q is even loaded.
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue_tile(s);
+    if (s < ntiles) issue_tile(s, s);
 
   bf16x8 qf[KSTEPS];
   load_q_frags<D, MT>(p.q + (row_base + my_rc) * D, kg, qf);
@@ -250,7 +268,40 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   float m_run = kNegBig;
   float l_run = 0.0f;
 
-  for (int it = 0; it < ntiles; ++it) {
+  // Per-lane LDS offsets, fixed for the whole loop: the swizzle depends only on
+  // the low 4 row bits, so moving by whole 16-row blocks or by whole swizzle
+  // periods of head-dim columns adds a constant that the instructions carry as
+  // an immediate.
+  constexpr int KSW = CPR_LOG2<D / 8>::value;          // swizzled chunk-index bits
+  constexpr int KPER_RAW = (1 << KSW) / (M::kK / 8);   // K-read column period in k-steps
+  constexpr int KPER = KPER_RAW < 1 ? 1 : (KPER_RAW > KSTEPS ? KSTEPS : KPER_RAW);
+  constexpr int VPER_RAW = (1 << KSW) / (MT / 8);      // V-read column period in d-blocks
+  constexpr int VPER = VPER_RAW < 1 ? 1 : (VPER_RAW > DBLK ? DBLK : VPER_RAW);
+  constexpr int VROWS = (MT == 32) ? 2 : 1;            // distinct row phases of a V read pair
+  int koff[KPER];
+#pragma unroll
+  for (int s = 0; s < KPER; ++s) {
+    const int col = s * M::kK + 8 * kg;
+    koff[s] = tile_off<D>(lane % MT, col < D ? col : 0);
+  }
+  uint32_t voff[VROWS][VPER];  // bytes
+  {
+    const int grp = lane >> 4, tj = (lane >> 2) & 3, ta = lane & 3;
+#pragma unroll
+    for (int db = 0; db < VPER; ++db) {
+      int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
+      if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
+      // MT = 32: k-slots 0..3 <-> keys 16*step + 4h + 0..3, 4..7 <-> 16*step + 8 + 4h + 0..3
+      // MT = 16: k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
+      const int row1 = (MT == 32) ? 4 * (grp >> 1) + tj : 4 * grp + tj;
+      voff[0][db] = 2u * tile_off<D>(row1, col);
+      if constexpr (VROWS == 2) voff[VROWS - 1][db] = 2u * tile_off<D>(row1 + 8, col);
+    }
+  }
+  const uint32_t v_lds = lds_addr((const FMHA_LDS void*)&smem[kV][0][0]);
+
+  auto tile = [&](auto stage_c, int it) {
+    constexpr int STG = decltype(stage_c)::value;
     const int t0 = kbeg + it * KT;
     // This wave's copies of tile `it` have landed (later tiles may still fly),
     // every wave is past its reads of tile it-1, and then everyone's copies of
@@ -258,17 +309,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     wait_tiles<kPerTile, STAGES - 2>(min(STAGES - 2, ntiles - 1 - it));
     wait_lgkmcnt0();
     lds_barrier();
-    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1);
+    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (STG + STAGES - 1) % STAGES);
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
-    if (CAUSAL && t0 > wave_max_last) continue;
-
-    const uint16_t* ks = &smem[it % STAGES][0][0];
-    const uint16_t* vs = &smem[it % STAGES][1][0];
+    if (CAUSAL && t0 > wave_max_last) return;
 
     // ---- S^T = K Q^T ----
+    const uint16_t* ks = &smem[kK][STG][0];
+    u32x4 kf[KBLK][KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        kf[kb][s] = lds_read_b128((const FMHA_LDS void*)&ks[kb * MT * D + koff[s % KPER] +
+                                                            (s / KPER) * KPER * M::kK]);
     Acc sacc[KBLK];
-    qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb) sacc[kb] = Acc{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+        sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[kb][s]), qf[s], sacc[kb]);
 
     // ---- mask the ragged end and the causal diagonal ----
     const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
@@ -309,44 +371,63 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     l_run += psum;
 
     // ---- O^T += V^T P^T ----
-    // Source-lane coordinates for the transpose read.
-    const int grp = lane >> 4;
-    const int tj = (lane >> 2) & 3;
-    const int ta = lane & 3;
+    // P as the B operand: k-slot e of a lane group holds the key that the S^T
+    // register layout put there (the key <-> k-slot map is noted at voff).
+    bf16x8 pb[NPV];
 #pragma unroll
     for (int step = 0; step < NPV; ++step) {
-      // Probabilities as the B operand: k-slot e of lane group g.
       u32x4 pw;
-      int row1, row2;
       if constexpr (MT == 32) {
         const int kb = step >> 1, t2 = step & 1;
         pw[0] = pack_bf16x2(sacc[kb][8 * t2 + 0], sacc[kb][8 * t2 + 1]);
         pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
         pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
         pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
-        // k-slots 0..3 <-> keys kofs + 4h + 0..3, slots 4..7 <-> kofs + 8 + 4h + 0..3
-        row1 = kb * 32 + 16 * t2 + 4 * (grp >> 1) + tj;
-        row2 = row1 + 8;
       } else {
-        const int kb0 = 2 * step, kb1 = 2 * step + 1;
-        pw[0] = pack_bf16x2(sacc[kb0][0], sacc[kb0][1]);
-        pw[1] = pack_bf16x2(sacc[kb0][2], sacc[kb0][3]);
-        pw[2] = pack_bf16x2(sacc[kb1][0], sacc[kb1][1]);
-        pw[3] = pack_bf16x2(sacc[kb1][2], sacc[kb1][3]);
-        // k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
-        row1 = 32 * step + 4 * grp + tj;
-        row2 = row1 + 16;
+        pw[0] = pack_bf16x2(sacc[2 * step][0], sacc[2 * step][1]);
+        pw[1] = pack_bf16x2(sacc[2 * step][2], sacc[2 * step][3]);
+        pw[2] = pack_bf16x2(sacc[2 * step + 1][0], sacc[2 * step + 1][1]);
+        pw[3] = pack_bf16x2(sacc[2 * step + 1][2], sacc[2 * step + 1][3]);
       }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
-        if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
-        const u32x2 lo = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row1, col)]);
-        const u32x2 hi = lds_read_tr16((const FMHA_LDS void*)&vs[tile_off<D>(row2, col)]);
-        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = M::run(__builtin_bit_cast(bf16x8, va), pb, oacc[db]);
-      }
+      pb[step] = __builtin_bit_cast(bf16x8, pw);
+    }
+    // V^T as the A operand through transpose reads, RA units (one MFMA each)
+    // ahead of the MFMAs.
+    constexpr int NU = NPV * DBLK;
+    constexpr int RA = NU < 4 ? NU : 4;
+    u32x4 vfrag[NU];
+    auto issue_v = [&](auto u_c) {
+      constexpr int U = decltype(u_c)::value;
+      constexpr int step = U / DBLK, db = U % DBLK;
+      constexpr uint32_t stage_bytes = (uint32_t)STG * TILE_ELEMS * 2;
+      constexpr uint32_t row_step = (MT == 32) ? 16u * D * 2 : 32u * D * 2;
+      constexpr uint32_t col_step = (uint32_t)(db / VPER) * VPER * MT * 2;
+      constexpr uint32_t imm1 = stage_bytes + step * row_step + col_step;
+      constexpr uint32_t imm2 = imm1 + ((MT == 32) ? 0u : 16u * D * 2);
+      const uint32_t a1 = v_lds + voff[0][db % VPER];
+      const uint32_t a2 = v_lds + voff[VROWS - 1][db % VPER];
+      const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
+      const u32x2 hi = lds_read_tr16_imm<imm2>(a2);
+      vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    static_for<0, RA>([&](auto u_c) { issue_v(u_c); });
+    static_for<0, NU>([&](auto u_c) {
+      constexpr int U = decltype(u_c)::value;
+      if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
+      constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
+      lds_wait_tied<pending>(vfrag[U]);
+      oacc[U % DBLK] = M::run(__builtin_bit_cast(bf16x8, vfrag[U]), pb[U / DBLK], oacc[U % DBLK]);
+    });
+  };
+
+  for (int it0 = 0; it0 < ntiles; it0 += STAGES) {
+    tile(std::integral_constant<int, 0>{}, it0);
+    if (it0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it0 + 1);
+    if constexpr (STAGES > 2) {
+      if (it0 + 2 < ntiles) tile(std::integral_constant<int, 2 % STAGES>{}, it0 + 2);
+    }
+    if constexpr (STAGES > 3) {
+      if (it0 + 3 < ntiles) tile(std::integral_constant<int, 3 % STAGES>{}, it0 + 3);
     }
   }
 

@@ -8,8 +8,9 @@
 #include <cstring>
 
 #include "../../include/fmha.h"
-#include "attn_kernels.hpp"
+#include "fmha_device.hpp"
 #include "host_common.hpp"
+#include "launch.hpp"
 
 namespace fmha {
 
@@ -36,21 +37,6 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Tile configuration of the decode kernel for a head dim and a row count.
-struct DecodeCfg {
-  int nw;  // waves per workgroup (16 query rows each)
-  int kt;  // keys per tile
-};
-
-// One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
-// small workgroups keep enough loads in flight per CU); four waves otherwise.
-// Head dim 512 always uses four waves sharing a 32-key, 2-stage ring (128 KB).
-DecodeCfg decode_cfg(int D, int rows_per_kv) {
-  if (D == 512) return {4, 32};
-  if (rows_per_kv <= 16) return {1, 32};
-  return {4, 64};
-}
-
 bool decode_dim_ok(int D) { return D == 64 || D == 128 || D == 512; }
 bool fwd_dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -72,71 +58,13 @@ fmha_status check_common(const void* q, const void* k, const void* v, const void
 }
 
 bool sizes_fit(long long B, long long Hq, long long Hkv, long long Sq, long long Sk, long long D) {
-  // 64-bit element offsets are used throughout; keep every tensor below 2^62 bytes and the
-  // grid within HIP's limits.
-  return B * Hq * Sq * D < (1LL << 61) && B * Hkv * Sk * D < (1LL << 61) && B <= 65535 &&
-         Hkv <= 65535;
+  // 64-bit element offsets are used throughout; keep every tensor below 2^61 elements.
+  return B * Hq * Sq * D < (1LL << 61) && B * Hkv * Sk * D < (1LL << 61);
 }
 
-template <int D, int MT, int NW, int KT, int ST, bool C, bool S>
-fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, ST, C, S>), grid, dim3(NW * 64), 0, st, p);
-  return check_launch("attention kernel launch");
-}
-
-template <int D, int MT, int NW, int KT, int ST>
-fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
-                           hipStream_t st) {
-  if (causal)
-    return split ? launch_attn<D, MT, NW, KT, ST, true, true>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, ST, true, false>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, ST, false, true>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, ST, false, false>(p, grid, st);
-}
-
-// Prefill: 4 waves of 32 rows = 128 query rows per workgroup, 64-key tiles in
-// a 3-stage LDS ring (2 stages at head dim 128).
-fmha_status dispatch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
-  switch (D) {
-    case 16: return launch_attn_cs<16, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 32: return launch_attn_cs<32, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 64: return launch_attn_cs<64, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 128: return launch_attn_cs<128, 32, 4, 64, 2>(p, grid, causal, false, st);
-  }
-  return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dim %d not built", D);
-}
-
-fmha_status dispatch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
-                            bool split, hipStream_t st) {
-  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 32, 3>(p, grid, causal, split, st);
-  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64, 2>(p, grid, causal, split, st);
-  if (D == 512) return launch_attn_cs<512, 16, 4, 32, 2>(p, grid, causal, split, st);
-  return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
-}
-
-fmha_status dispatch_combine(int D, const float* op, const float* lp, uint16_t* o, float* lse,
-                             float* amax, long long nrows, int nsplit, hipStream_t st) {
-  const int rows_per_block = 4;
-  dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
-  switch (D) {
-    case 64:
-      hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
-      break;
-    case 128:
-      hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
-      break;
-    case 512:
-      hipLaunchKernelGGL(lse_combine_kernel<512>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
-      break;
-    default:
-      return fail(FMHA_ERR_HEAD_DIM, "combine: head dim %d not built", D);
-  }
-  return check_launch("combine kernel launch");
+// The kernels index a 1-D grid with 32-bit ints.
+bool grid_fits(long long row_blocks, long long splits, long long Hkv, long long B) {
+  return row_blocks * splits * Hkv * B < (1LL << 31);
 }
 
 int num_cus() {
@@ -211,6 +139,7 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.v = (const uint16_t*)v;
   p.o = (uint16_t*)o;
   p.lse = lse;
+  p.B = B;
   p.Hkv = Hkv;
   p.Sq = Sq;
   p.Sk = Sk;
@@ -219,8 +148,9 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.nsplit = 1;
   p.split_len = (Sk + 63) / 64 * 64;
   p.scale_log2 = scale * kLog2e;
-  dim3 grid(p.n_row_blocks, Hkv, B);
-  return dispatch_fwd(D, p, grid, causal != 0, (hipStream_t)stream);
+  if (!grid_fits(p.n_row_blocks, 1, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
+  dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
+  return launch_fwd(D, p, grid, causal != 0, (hipStream_t)stream);
 }
 
 int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
@@ -267,6 +197,7 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   p.o = (uint16_t*)o;
   p.lse = lse;
   p.o_amax = o_amax;
+  p.B = B;
   p.Hkv = Hkv;
   p.Sq = Sq;
   p.Sk = Sk;
@@ -276,10 +207,11 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   p.split_len = split_len;
   p.scale_log2 = scale * kLog2e;
   const hipStream_t st = (hipStream_t)stream;
+  if (!grid_fits(p.n_row_blocks, ns_eff, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
 
   if (ns_eff <= 1) {
-    dim3 grid(p.n_row_blocks, Hkv, B);
-    return dispatch_decode(D, c, p, grid, causal != 0, false, st);
+    dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
+    return launch_decode(D, c, p, grid, causal != 0, false, st);
   }
 
   const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns);
@@ -290,10 +222,10 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   const size_t rows = (size_t)B * Hq * Sq;
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + round_up(rows * ns * D * sizeof(float), kAlign));
-  dim3 grid(p.n_row_blocks * ns_eff, Hkv, B);
-  s = dispatch_decode(D, c, p, grid, causal != 0, true, st);
+  dim3 grid((unsigned)p.n_row_blocks * ns_eff * Hkv * B);
+  s = launch_decode(D, c, p, grid, causal != 0, true, st);
   if (s != FMHA_OK) return s;
-  return dispatch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, (long long)rows,
+  return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, (long long)rows,
                           ns_eff, st);
 }
 
@@ -305,19 +237,8 @@ fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int
     return fail(FMHA_ERR_SHAPE, "debug scores need 1 <= Sq, Sk <= 128");
   if (!aligned16(q) || !aligned16(k) || !aligned16(s_out))
     return fail(FMHA_ERR_ALIGN, "q, k and s_out must be 16-byte aligned");
-  const hipStream_t st = (hipStream_t)stream;
-  switch (D) {
-    case 16: hipLaunchKernelGGL(qk_scores_debug_kernel<16>, dim3(1), dim3(256), 0, st,
-                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
-    case 32: hipLaunchKernelGGL(qk_scores_debug_kernel<32>, dim3(1), dim3(256), 0, st,
-                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
-    case 64: hipLaunchKernelGGL(qk_scores_debug_kernel<64>, dim3(1), dim3(256), 0, st,
-                                (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
-    case 128: hipLaunchKernelGGL(qk_scores_debug_kernel<128>, dim3(1), dim3(256), 0, st,
-                                 (const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, scale); break;
-    default: return fail(FMHA_ERR_HEAD_DIM, "debug scores support D in {16,32,64,128}");
-  }
-  return check_launch("debug score kernel launch");
+  return launch_debug_scores((const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, D, scale,
+                             (hipStream_t)stream);
 }
 
 }  // extern "C"

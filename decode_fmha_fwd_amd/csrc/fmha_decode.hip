@@ -1,0 +1,63 @@
+// fmha_decode.hip -- instantiations and launchers of the split-KV decode
+// attention kernels (16-row waves) and of the log-sum-exp combine kernel.
+#include <hip/hip_runtime.h>
+
+#include "attn_kernels.hpp"
+#include "host_common.hpp"
+#include "launch.hpp"
+
+namespace fmha {
+namespace {
+
+template <int D, int MT, int NW, int KT, int ST, bool C, bool S>
+fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, ST, C, S>), grid, dim3(NW * 64), 0, st, p);
+  return check_launch("attention kernel launch");
+}
+
+template <int D, int MT, int NW, int KT, int ST>
+fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
+                           hipStream_t st) {
+  if (causal)
+    return split ? launch_attn<D, MT, NW, KT, ST, true, true>(p, grid, st)
+                 : launch_attn<D, MT, NW, KT, ST, true, false>(p, grid, st);
+  return split ? launch_attn<D, MT, NW, KT, ST, false, true>(p, grid, st)
+               : launch_attn<D, MT, NW, KT, ST, false, false>(p, grid, st);
+}
+
+}  // namespace
+
+fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
+                            bool split, hipStream_t st) {
+  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 32, 3>(p, grid, causal, split, st);
+  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64, 2>(p, grid, causal, split, st);
+  if (D == 512) return launch_attn_cs<512, 16, 4, 32, 2>(p, grid, causal, split, st);
+  return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
+}
+
+fmha_status launch_combine(int D, const float* op, const float* lp, uint16_t* o, float* lse,
+                           float* amax, long long nrows, int nsplit, hipStream_t st) {
+  const int rows_per_block = 4;
+  dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    case 128:
+      hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    case 512:
+      hipLaunchKernelGGL(lse_combine_kernel<512>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
+                         nrows, nsplit);
+      break;
+    default:
+      return fail(FMHA_ERR_HEAD_DIM, "combine: head dim %d not built", D);
+  }
+  return check_launch("combine kernel launch");
+}
+
+}  // namespace fmha

@@ -72,12 +72,14 @@ template <> __device__ inline int acc_row<32>(int lane, int r) {
 }
 template <> __device__ inline int acc_row<16>(int lane, int r) { return 4 * (lane >> 4) + r; }
 
-// Two floats -> two bf16 (round to nearest even, the hardware conversion)
-// packed low/high into one dword.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) packed low/high into one
+// dword: a single v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ inline float bf16_bits_to_float(uint32_t h) {
@@ -119,6 +121,38 @@ __device__ inline u32x2 lds_read_tr16(const FMHA_LDS void* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FMHA_LDS i16x4*)p);
   return __builtin_bit_cast(u32x2, r);
 }
+
+// The same transpose read issued from inline asm.  The compiler cannot tell
+// which LDS bytes a transpose-read builtin touches, so it would wait for every
+// outstanding global->LDS copy (vmcnt(0)) before each one, serialising the
+// prefetch ring; from asm it inserts nothing, and the caller must wait with
+// lds_wait_tied before using the result.
+__device__ inline u32x2 lds_read_tr16_async(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+
+// The transpose read with a constant LDS byte offset folded into the
+// instruction (offset < 64 KiB).
+template <uint32_t OFF>
+__device__ inline u32x2 lds_read_tr16_imm(uint32_t lds_addr) {
+  static_assert(OFF < 65536u, "DS offset field is 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N) tied to a register tuple, so the compiler cannot use
+// the tuple before the wait.  LDS operations complete in order, so waiting for
+// at most N outstanding means everything issued before the last N is done.
+template <int N>
+__device__ inline void lds_wait_tied(u32x4& r) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+
+__device__ inline uint32_t lds_addr(const FMHA_LDS void* p) { return (uint32_t)(size_t)p; }
 
 __device__ inline u32x4 lds_read_b128(const FMHA_LDS void* p) {
   return *(const FMHA_LDS u32x4*)p;

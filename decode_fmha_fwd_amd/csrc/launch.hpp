@@ -1,0 +1,59 @@
+// launch.hpp -- the parameter block of the attention kernels and the host
+// launchers each kernel translation unit provides to the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fmha.h"
+
+namespace fmha {
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;          // bf16 output (no split)
+  float* lse;           // fp32 [rows] or null (no split)
+  float* o_part;        // fp32 [rows][nsplit][D] (split)
+  float* lse_part;      // fp32 [rows][nsplit]   (split)
+  float* o_amax;        // optional running max |O| (no split)
+  int B;
+  int Hkv;
+  int Sq;
+  int Sk;
+  int rows_per_kv;      // (Hq / Hkv) * Sq query rows share one KV head
+  int n_row_blocks;     // ceil(rows_per_kv / (NW * MT))
+  int nsplit;           // key ranges per (batch, KV head)
+  int split_len;        // keys per range, a multiple of KT
+  float scale_log2;     // scale * log2(e)
+};
+
+// Tile configuration of the decode kernel for a head dim and a row count.
+struct DecodeCfg {
+  int nw;  // waves per workgroup (16 query rows each)
+  int kt;  // keys per tile
+};
+
+// One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
+// small workgroups keep enough loads in flight per CU); four waves otherwise.
+// Head dim 512 always uses four waves sharing a 32-key, 2-stage ring (128 KB).
+inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
+  if (D == 512) return {4, 32};
+  if (rows_per_kv <= 16) return {1, 32};
+  return {4, 64};
+}
+
+// fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).
+fmha_status launch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st);
+fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_out, int Sq,
+                                int Sk, int D, float scale, hipStream_t st);
+
+// fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
+fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
+                          bool split, hipStream_t st);
+fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,
+                           float* lse, float* o_amax, long long nrows, int nsplit,
+                           hipStream_t st);
+
+}  // namespace fmha
