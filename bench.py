@@ -23,6 +23,10 @@ import sys
 import time
 
 METRIC = "FMHA TFLOP/s (prefill) and KV GB/s (decode) at hd=64/512 on 1 MI355X"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["attn_kernels.hpp", "fmha_device.hpp", "launch.hpp", "fmha_prefill.hip",
+                  "fmha_decode.hip", "nvfp4.hip", "fmha_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_workloads.md")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 
@@ -114,6 +118,33 @@ def time_workload(w, dev, steps, warmup):
     del r
     torch.cuda.empty_cache()
     return total_ms / steps, per, wall
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_fmha_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's attention kernel, as read by the
+    rocprofv3 FETCH_SIZE/WRITE_SIZE counters (scaled by a copy-kernel
+    calibration) and recorded in profiles/; None when the kernel sources have
+    changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    sha = kernel_source_sha()
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 5 and parts[0] == "traffic_bytes_per_launch" and parts[1] == workload:
+            return int(parts[2]) if parts[4] == sha else None
+    return None
 
 
 def summarise(w, ms):
@@ -210,13 +241,15 @@ def main():
     if head.kind == "fwd":
         achieved = head.flops() / (kernel_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(head.name),
                 "kernel": "attn_fwd_kernel<64,32,4,64,causal>", "kernel_ms_median": round(kernel_ms, 5)}
         value, unit = s["tflops"], "TFLOP/s"
     else:
         achieved = head.bytes() / (kernel_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(head.name),
                 "kernel_ms_median": round(kernel_ms, 5)}
         value, unit = s["kv_gbs"], "GB/s"
 

@@ -128,7 +128,7 @@ __device__ inline void qk_scores(const uint16_t* ks,
 // w fills the contiguous LDS slots [(j*NW + w)*64, +64) and every lane fetches
 // the global bytes that belong in its slot, so 8 lanes read one 128-byte row
 // segment and the swizzle costs nothing on the HBM side.
-template <int D, int NW, int KT>
+template <int D, int NW, int KT, bool NT>
 struct TileCopy {
   static constexpr int kTileBytes = KT * D * 2;
   static constexpr int kBytes = (kTileBytes >= NW * 64 * 16) ? 16 : 4;
@@ -149,7 +149,7 @@ struct TileCopy {
       const int lchunk = pchunk ^ swz<CPR>(row);
       const long long key = min(t0 + row, Sk - 1);
       const uint16_t* g = base + key * D + lchunk * 8 + ((inrow & 15) >> 1);
-      dma_to_lds<kBytes>(g, (FMHA_LDS void*)(lds + (j * NW + wave) * 64 * kBytes));
+      dma_to_lds<kBytes, NT>(g, (FMHA_LDS void*)(lds + (j * NW + wave) * 64 * kBytes));
     }
   }
 };
@@ -177,16 +177,20 @@ template <int D, int MT, int NW, int KT, int STAGES, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
-  using Copy = TileCopy<D, NW, KT>;
+  // Decode reads every K/V byte once: stream it non-temporally.  Prefill
+  // re-reads K/V from L2 for every row block of a head: keep it cached.
+  using Copy = TileCopy<D, NW, KT, /*NT=*/MT == 16>;
   constexpr int KSTEPS = (D + M::kK - 1) / M::kK;  // QK contraction steps
   constexpr int KBLK = KT / MT;                    // MT-key blocks per tile
   constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
   constexpr int ROWS_WG = NW * MT;
-  constexpr int NPV = (MT == 32) ? 2 * KBLK : KBLK / 2;  // PV instructions per d-block
+  // PV instructions per d-block; a 16-row wave consumes 32 keys per PV
+  // instruction, so a 16-key tile fills half of one (the other half gets P = 0).
+  constexpr int NPV = (MT == 32) ? 2 * KBLK : (KBLK + 1) / 2;
   constexpr int TILE_ELEMS = KT * D;
   constexpr int kPerTile = 2 * Copy::kLoads;       // copies per wave per tile (K and V)
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
-  static_assert(MT == 32 || KT % 32 == 0, "16-row waves consume 32 keys per PV step");
+  static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
   static_assert(D % 16 == 0 && D >= 16, "head dim must be a multiple of 16");
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
   static_assert(kPerTile * (STAGES - 2) < 64, "vmcnt range");
@@ -386,8 +390,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       } else {
         pw[0] = pack_bf16x2(sacc[2 * step][0], sacc[2 * step][1]);
         pw[1] = pack_bf16x2(sacc[2 * step][2], sacc[2 * step][3]);
-        pw[2] = pack_bf16x2(sacc[2 * step + 1][0], sacc[2 * step + 1][1]);
-        pw[3] = pack_bf16x2(sacc[2 * step + 1][2], sacc[2 * step + 1][3]);
+        if (2 * step + 1 < KBLK) {
+          pw[2] = pack_bf16x2(sacc[2 * step + 1][0], sacc[2 * step + 1][1]);
+          pw[3] = pack_bf16x2(sacc[2 * step + 1][2], sacc[2 * step + 1][3]);
+        } else {
+          pw[2] = 0u;
+          pw[3] = 0u;
+        }
       }
       pb[step] = __builtin_bit_cast(bf16x8, pw);
     }
@@ -403,7 +412,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       constexpr uint32_t row_step = (MT == 32) ? 16u * D * 2 : 32u * D * 2;
       constexpr uint32_t col_step = (uint32_t)(db / VPER) * VPER * MT * 2;
       constexpr uint32_t imm1 = stage_bytes + step * row_step + col_step;
-      constexpr uint32_t imm2 = imm1 + ((MT == 32) ? 0u : 16u * D * 2);
+      // (a half-filled 16-key step re-reads its own rows for the zero-P half)
+      constexpr uint32_t imm2 = imm1 + ((MT == 32 || KT == 16) ? 0u : 16u * D * 2);
       const uint32_t a1 = v_lds + voff[0][db % VPER];
       const uint32_t a2 = v_lds + voff[VROWS - 1][db % VPER];
       const u32x2 lo = lds_read_tr16_imm<imm1>(a1);

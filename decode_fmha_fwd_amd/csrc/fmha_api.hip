@@ -92,12 +92,10 @@ int default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   const DecodeCfg c = decode_cfg(D, rows);
   const long long n_rb = (rows + 16 * c.nw - 1) / (16 * c.nw);
   const long long units = (long long)B * Hkv * n_rb;
-  // Aim for about 8 resident waves per CU, keep at least 4 tiles per split.
-  const long long want_waves = 8LL * num_cus();
+  // Fill every workgroup slot of the GPU once; keep at least 4 tiles per split.
+  const long long want_wgs = (long long)c.wgs_per_cu * num_cus();
   int ns = 1;
-  while ((long long)ns * units * c.nw < want_waves && ns < 1024 &&
-         Sk / (2 * ns) >= 4 * c.kt)
-    ns *= 2;
+  while ((long long)ns * units < want_wgs && ns < 1024 && Sk / (2 * ns) >= 4 * c.kt) ns *= 2;
   return ns;
 }
 

@@ -33,7 +33,7 @@ fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bo
   if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3>(p, grid, causal, split, st);
   if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2>(p, grid, causal, split, st);
   if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64, 2>(p, grid, causal, split, st);
-  if (D == 512) return launch_attn_cs<512, 16, 4, 32, 2>(p, grid, causal, split, st);
+  if (D == 512) return launch_attn_cs<512, 16, 4, 16, 4>(p, grid, causal, split, st);
   return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
 }
 

@@ -31,17 +31,20 @@ struct AttnParams {
 
 // Tile configuration of the decode kernel for a head dim and a row count.
 struct DecodeCfg {
-  int nw;  // waves per workgroup (16 query rows each)
-  int kt;  // keys per tile
+  int nw;          // waves per workgroup (16 query rows each)
+  int kt;          // keys per tile
+  int wgs_per_cu;  // workgroups one CU holds at once (LDS-limited)
 };
 
 // One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
 // small workgroups keep enough loads in flight per CU); four waves otherwise.
-// Head dim 512 always uses four waves sharing a 32-key, 2-stage ring (128 KB).
+// Head dim 512 always uses four waves sharing a 16-key, 4-stage ring (128 KB,
+// three tiles in flight).
+// Must match the instantiations in fmha_decode.hip.
 inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
-  if (D == 512) return {4, 32};
-  if (rows_per_kv <= 16) return {1, 32};
-  return {4, 64};
+  if (D == 512) return {4, 16, 1};
+  if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 5};
+  return {4, 64, D == 64 ? 3 : 2};
 }
 
 // fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).
