@@ -8,6 +8,12 @@ turned off for all device code; the NVFP4 translation unit additionally keeps
 fp contraction off, correctly rounded fp32 division and fp32 denormals,
 because it decides integer codes; the prefill kernels keep MFMA accumulators
 in ordinary VGPRs.
+
+The attention translation units issue some LDS reads from inline asm; their
+device assembly is kept from the compile (``-save-temps``) and checked by
+``asm_check`` before the library is linked, so a build in which register
+allocation touched such a read's result before its wait fails here instead of
+computing with stale data.
 """
 from __future__ import annotations
 
@@ -16,6 +22,11 @@ import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+try:
+    from . import asm_check
+except ImportError:  # run as a script
+    import asm_check
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -34,6 +45,7 @@ PER_FILE = {
                   "-fno-gpu-flush-denormals-to-zero"],
 }
 SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "nvfp4.hip"]
+ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip"}
 
 
 def hipcc() -> str:
@@ -46,9 +58,24 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [hipcc(), *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    tmp = None
+    if src in ASM_CHECKED:
+        tmp = os.path.join(BUILD, "temps_" + src.replace(".hip", ""))
+        shutil.rmtree(tmp, ignore_errors=True)
+        os.makedirs(tmp)
+        cmd.append("-save-temps")
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    if tmp is not None:
+        asm = [f for f in os.listdir(tmp) if f.endswith(f"-hip-amdgcn-amd-amdhsa-{ARCH}.s")]
+        if len(asm) != 1:
+            raise RuntimeError(f"device assembly of {src} not found in {tmp}")
+        rep = asm_check.check_file(os.path.join(tmp, asm[0]))
+        if rep.problems:
+            raise RuntimeError(f"{src}: inline-asm LDS read hazard(s):\n" +
+                               "\n".join(rep.problems[:10]))
+        shutil.rmtree(tmp, ignore_errors=True)
     return obj
 
 

@@ -14,9 +14,9 @@
 //     (MT = 32 or 16 rows per wave).  Rows are the flattened (grouped head,
 //     position) pairs of that KV head, so GQA decode packs all Hq/Hkv heads of
 //     a KV head into one workgroup and each K/V byte is read once.
-//   * K and V tiles of KT keys stream from HBM straight into a ring of STAGES
-//     LDS tiles with asynchronous global->LDS copies (no registers, issued
-//     STAGES-1 tiles ahead, one barrier per tile); 16-byte chunks are
+//   * K and V tiles of KT keys stream from HBM straight into rings of KST and
+//     VST LDS tiles with asynchronous global->LDS copies (no registers, issued
+//     KST-1 / VST-1 tiles ahead, one barrier per tile); 16-byte chunks are
 //     XOR-swizzled by row so MFMA operand reads are free of bank conflicts.
 //   * Scores are computed transposed, S^T = K * Q^T (K is the A operand, Q^T
 //     the B operand held in registers), so each lane owns ONE query row and a
@@ -28,6 +28,12 @@
 //   * Online softmax in base 2: m is kept in units of log2, p = exp2(s*c - m)
 //     with c = scale*log2(e) folded into one FMA; the output rescale factor is
 //     exp2(m_old - m_new).
+//   * Every LDS read of the tile loop (K operand reads and V transpose reads)
+//     is issued from inline asm and waited for with explicit lgkmcnt waits: a
+//     compiler-visible LDS read placed after asynchronous global->LDS copies
+//     makes the compiler drain every copy in flight (vmcnt(0)) first, which
+//     would serialise the ring.  The build scans the generated assembly to
+//     prove no result of such a read is touched before its wait.
 #pragma once
 
 #include <climits>
@@ -122,49 +128,52 @@ __device__ inline void qk_scores(const uint16_t* ks,
       sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[kb][s]), qf[s], sacc[kb]);
 }
 
-// Copies one K or V tile (KT rows of D bf16, rows clamped to the last key for
-// a ragged tail) into a swizzled LDS tile with asynchronous global->LDS
-// copies.  Each wave issues kLoads copies of 64 lanes x BYTES; copy j of wave
-// w fills the contiguous LDS slots [(j*NW + w)*64, +64) and every lane fetches
-// the global bytes that belong in its slot, so 8 lanes read one 128-byte row
-// segment and the swizzle costs nothing on the HBM side.
-template <int D, int NW, int KT, bool NT>
+// Copies one K or V tile (KT rows of W bf16 taken at column col0 of rows that
+// are `stride` elements apart; rows clamped to the last key for a ragged tail)
+// into a swizzled LDS tile with asynchronous global->LDS copies.  Each wave
+// issues kLoads copies of 64 lanes x BYTES; copy j of wave w fills the
+// contiguous LDS slots [(j*NW + w)*64, +64) and every lane fetches the global
+// bytes that belong in its slot, so 8 lanes read one 128-byte row segment and
+// the swizzle costs nothing on the HBM side.
+template <int W, int NW, int KT, bool NT>
 struct TileCopy {
-  static constexpr int kTileBytes = KT * D * 2;
+  static constexpr int kTileBytes = KT * W * 2;
   static constexpr int kBytes = (kTileBytes >= NW * 64 * 16) ? 16 : 4;
   static constexpr int kLoads = kTileBytes / (NW * 64 * kBytes);
   static_assert(kLoads >= 1 && kLoads * NW * 64 * kBytes == kTileBytes,
                 "tile must split evenly over the workgroup's copies");
 
-  __device__ static inline void issue(const uint16_t* base, int t0, int Sk, FMHA_LDS char* lds,
-                                      int wave, int lane) {
-    constexpr int CPR = D / 8;
+  __device__ static inline void issue(const uint16_t* base, int stride, int col0, int t0, int Sk,
+                                      FMHA_LDS char* lds, int wave, int lane) {
+    constexpr int CPR = W / 8;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int slot = (j * NW + wave) * 64 + lane;
       const int byte = slot * kBytes;
-      const int row = byte / (D * 2);
-      const int inrow = byte - row * (D * 2);
+      const int row = byte / (W * 2);
+      const int inrow = byte - row * (W * 2);
       const int pchunk = inrow >> 4;
       const int lchunk = pchunk ^ swz<CPR>(row);
       const long long key = min(t0 + row, Sk - 1);
-      const uint16_t* g = base + key * D + lchunk * 8 + ((inrow & 15) >> 1);
+      const uint16_t* g = base + key * stride + col0 + lchunk * 8 + ((inrow & 15) >> 1);
       dma_to_lds<kBytes, NT>(g, (FMHA_LDS void*)(lds + (j * NW + wave) * 64 * kBytes));
     }
   }
 };
 
-// Waits until at most `pending` tiles (each kPerTile copies) of this wave's
-// copies are still in flight.
-template <int kPerTile, int kMaxPending>
-__device__ inline void wait_tiles(int pending) {
-  if constexpr (kMaxPending >= 2) {
-    if (pending >= 2) { wait_vmcnt<2 * kPerTile>(); return; }
+// s_waitcnt vmcnt(<= n) for a run-time n in [0, N]: waits for the largest
+// immediate not above n (waiting for fewer outstanding copies is always safe).
+template <int N>
+__device__ inline void wait_vmcnt_at_most(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N>();
+      return;
+    }
+    wait_vmcnt_at_most<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (kMaxPending >= 1) {
-    if (pending >= 1) { wait_vmcnt<kPerTile>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
 // Lazy rescaling threshold (log2 units): the running maximum only moves when
@@ -173,32 +182,42 @@ __device__ inline void wait_tiles(int pending) {
 // and bf16.  The final O / l and LSE are exact whichever maximum is used.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int MT, int NW, int KT, int STAGES, bool CAUSAL, bool SPLIT>
+// KST / VST: depth of the K and V rings (VST <= KST <= VST + 1).  V is read
+// after K within a tile, so with one K stage more than V stages the extra
+// look-ahead costs a K tile of LDS rather than a K and a V tile.
+template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
   // Decode reads every K/V byte once: stream it non-temporally.  Prefill
   // re-reads K/V from L2 for every row block of a head: keep it cached.
-  using Copy = TileCopy<D, NW, KT, /*NT=*/MT == 16>;
+  constexpr bool kStream = (MT == 16);
+  using Copy = TileCopy<D, NW, KT, kStream>;
   constexpr int KSTEPS = (D + M::kK - 1) / M::kK;  // QK contraction steps
   constexpr int KBLK = KT / MT;                    // MT-key blocks per tile
   constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
   constexpr int ROWS_WG = NW * MT;
-  // PV instructions per d-block; a 16-row wave consumes 32 keys per PV
-  // instruction, so a 16-key tile fills half of one (the other half gets P = 0).
-  constexpr int NPV = (MT == 32) ? 2 * KBLK : (KBLK + 1) / 2;
+  // PV instructions per d-block: 16 keys each for 32-row waves, 32 keys each
+  // for 16-row waves -- except 16-key tiles, which use the 16x16x16 MFMA.
+  constexpr bool kPV16 = (MT == 16 && KT == 16);
+  constexpr int NPV = (MT == 32) ? 2 * KBLK : (kPV16 ? 1 : (KBLK + 1) / 2);
   constexpr int TILE_ELEMS = KT * D;
   constexpr int kPerTile = 2 * Copy::kLoads;       // copies per wave per tile (K and V)
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
   static_assert(D % 16 == 0 && D >= 16, "head dim must be a multiple of 16");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
-  static_assert(kPerTile * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(VST >= 2 && KST <= 6 && (KST == VST || KST == VST + 1), "ring depths");
+  // copies of this wave that may still be in flight when a tile is needed
+  constexpr int kMaxPending = (KST == VST) ? (KST - 2) * kPerTile
+                                           : Copy::kLoads + (VST - 2) * kPerTile;
+  static_assert(kMaxPending < 64, "vmcnt range");
+  static_assert(VST * TILE_ELEMS * 2 <= 65536, "V ring must fit the 16-bit DS offset");
+  constexpr int LCM = (KST == VST) ? KST : KST * VST;  // loop unroll: both stages constant
 
-  // [K | V][stage][KT * D]: V tiles first in LDS so that every V transpose
-  // read can carry its full LDS offset as an instruction immediate (< 64 KiB).
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][STAGES][TILE_ELEMS];
-  constexpr int kV = 0, kK = 1;
+  // V ring first in LDS so that every V transpose read can carry its full LDS
+  // offset as an instruction immediate (< 64 KiB); then the K ring.
+  __shared__ __attribute__((aligned(16))) uint16_t vsm[VST][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t ksm[KST][TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,15 +272,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
 
-  auto issue_tile = [&](int it, int stage) {
-    Copy::issue(kbase, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&smem[kK][stage][0], wave, lane);
-    Copy::issue(vbase, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&smem[kV][stage][0], wave, lane);
+  auto issue_k = [&](int it, int stage) {
+    Copy::issue(kbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
+  };
+  auto issue_v = [&](int it, int stage) {
+    Copy::issue(vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
+  };
+  // Copies of this wave issued after both K(it) and V(it) (see the issue
+  // order: prologue V0 K0 V1 K1 ..., then per tile V(it+VST-1), K(it+KST-1)).
+  auto pending_after = [&](int it) {
+    int n = 0;
+    if constexpr (KST == VST) {
+#pragma unroll
+      for (int j = 1; j <= KST - 2; ++j)
+        if (it + j < ntiles) n += kPerTile;
+    } else {
+      if (it + 1 < ntiles) n += Copy::kLoads;
+#pragma unroll
+      for (int j = 1; j <= VST - 2; ++j) {
+        if (it + j < ntiles) n += Copy::kLoads;
+        if (it + j + 1 < ntiles) n += Copy::kLoads;
+      }
+    }
+    return n;
   };
 
-  // Prologue: the first STAGES-1 tiles in flight before Q is even loaded.
+  // Prologue: the first tiles in flight before Q is even loaded.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue_tile(s, s);
+  for (int s = 0; s < KST - 1; ++s) {
+    if (s < VST - 1 && s < ntiles) issue_v(s, s);
+    if (s < ntiles) issue_k(s, s);
+  }
 
   bf16x8 qf[KSTEPS];
   load_q_frags<D, MT>(p.q + (row_base + my_rc) * D, kg, qf);
@@ -282,12 +323,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int VPER_RAW = (1 << KSW) / (MT / 8);      // V-read column period in d-blocks
   constexpr int VPER = VPER_RAW < 1 ? 1 : (VPER_RAW > DBLK ? DBLK : VPER_RAW);
   constexpr int VROWS = (MT == 32) ? 2 : 1;            // distinct row phases of a V read pair
-  int koff[KPER];
+  uint32_t koff[KPER];  // bytes
 #pragma unroll
   for (int s = 0; s < KPER; ++s) {
     const int col = s * M::kK + 8 * kg;
-    koff[s] = tile_off<D>(lane % MT, col < D ? col : 0);
+    koff[s] = 2u * tile_off<D>(lane % MT, col < D ? col : 0);
   }
+  const uint32_t k_lds = lds_addr((const FMHA_LDS void*)&ksm[0][0]);
   uint32_t voff[VROWS][VPER];  // bytes
   {
     const int grp = lane >> 4, tj = (lane >> 2) & 3, ta = lane & 3;
@@ -302,39 +344,76 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       if constexpr (VROWS == 2) voff[VROWS - 1][db] = 2u * tile_off<D>(row1 + 8, col);
     }
   }
-  const uint32_t v_lds = lds_addr((const FMHA_LDS void*)&smem[kV][0][0]);
+  const uint32_t v_lds = lds_addr((const FMHA_LDS void*)&vsm[0][0]);
 
-  auto tile = [&](auto stage_c, int it) {
-    constexpr int STG = decltype(stage_c)::value;
+  auto tile = [&](auto u_c, int it) {
+    constexpr int U = decltype(u_c)::value;  // it % LCM
+    constexpr int KSG = U % KST, STG = U % VST;
     const int t0 = kbeg + it * KT;
     // This wave's copies of tile `it` have landed (later tiles may still fly),
     // every wave is past its reads of tile it-1, and then everyone's copies of
     // tile `it` are visible.
-    wait_tiles<kPerTile, STAGES - 2>(min(STAGES - 2, ntiles - 1 - it));
+    wait_vmcnt_at_most<kMaxPending>(pending_after(it));
     wait_lgkmcnt0();
     lds_barrier();
-    if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (STG + STAGES - 1) % STAGES);
+    if (it + VST - 1 < ntiles) issue_v(it + VST - 1, (U + VST - 1) % VST);
+    if (it + KST - 1 < ntiles) issue_k(it + KST - 1, (U + KST - 1) % KST);
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
     if (CAUSAL && t0 > wave_max_last) return;
 
     // ---- S^T = K Q^T ----
-    const uint16_t* ks = &smem[kK][STG][0];
-    u32x4 kf[KBLK][KSTEPS];
-#pragma unroll
-    for (int kb = 0; kb < KBLK; ++kb)
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        kf[kb][s] = lds_read_b128((const FMHA_LDS void*)&ks[kb * MT * D + koff[s % KPER] +
-                                                            (s / KPER) * KPER * M::kK]);
+    // K fragments are read in chunks of QCH contraction steps, one chunk ahead
+    // of the MFMAs that use it (bounded register footprint at large D; one
+    // step at a time for 32-row waves, whose register budget sets how many
+    // waves share a SIMD).
+    constexpr int QCH = (MT == 32) ? 1 : (KSTEPS < 4 ? KSTEPS : 4);
+    constexpr int NQC = (KSTEPS + QCH - 1) / QCH;
+    // Byte offset of this tile's K stage: an instruction immediate when the
+    // whole ring fits the 16-bit DS offset, else added once per tile.
+    constexpr uint32_t kStageBytes = (uint32_t)KSG * TILE_ELEMS * 2;
+    constexpr bool kStageImm = (uint32_t)KST * TILE_ELEMS * 2 <= 65536u;
+    const uint32_t kst = k_lds + (kStageImm ? 0u : kStageBytes);
+    u32x4 kf[NQC][KBLK][QCH];
+    auto read_k = [&](auto c_c) {
+      constexpr int C = decltype(c_c)::value;
+      static_for<0, KBLK * QCH>([&](auto j_c) {
+        constexpr int J = decltype(j_c)::value;
+        constexpr int kb = J / QCH, i = J % QCH, s = C * QCH + i;
+        if constexpr (s < KSTEPS) {
+          constexpr uint32_t imm = (kStageImm ? kStageBytes : 0u) +
+                                   2u * (kb * MT * D + (s / KPER) * KPER * M::kK);
+          kf[C][kb][i] = lds_read_b128_imm<imm>(kst + koff[s % KPER]);
+        }
+      });
+    };
     Acc sacc[KBLK];
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) sacc[kb] = Acc{};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+    read_k(std::integral_constant<int, 0>{});
+    static_for<0, NQC>([&](auto c_c) {
+      constexpr int C = decltype(c_c)::value;
+      if constexpr (C + 1 < NQC) read_k(std::integral_constant<int, C + 1>{});
+      // chunk C has landed once at most the next chunk's reads are in flight
+      constexpr int kNext = (C + 1 < NQC) ? KBLK * ((KSTEPS - (C + 1) * QCH) < QCH
+                                                        ? (KSTEPS - (C + 1) * QCH)
+                                                        : QCH)
+                                          : 0;
+      lds_wait<kNext>();
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb)
-        sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[kb][s]), qf[s], sacc[kb]);
+#pragma unroll
+        for (int i = 0; i < QCH; ++i)
+          if (C * QCH + i < KSTEPS) lds_tie(kf[C][kb][i]);
+#pragma unroll
+      for (int i = 0; i < QCH; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb) {
+          const int s = C * QCH + i;
+          if (s < KSTEPS)
+            sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[C][kb][i]), qf[s], sacc[kb]);
+        }
+    });
 
     // ---- mask the ragged end and the causal diagonal ----
     const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
@@ -387,15 +466,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
         pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
         pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
+      } else if constexpr (kPV16) {
+        pw[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);  // keys 4g + 0..3 (one 16x16x16)
+        pw[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
+        pw[2] = pw[3] = 0u;
       } else {
         pw[0] = pack_bf16x2(sacc[2 * step][0], sacc[2 * step][1]);
         pw[1] = pack_bf16x2(sacc[2 * step][2], sacc[2 * step][3]);
         if (2 * step + 1 < KBLK) {
           pw[2] = pack_bf16x2(sacc[2 * step + 1][0], sacc[2 * step + 1][1]);
           pw[3] = pack_bf16x2(sacc[2 * step + 1][2], sacc[2 * step + 1][3]);
-        } else {
-          pw[2] = 0u;
-          pw[3] = 0u;
+        } else {  // a 16-key tile on the 32-deep MFMA: the upper k-slots get P = 0
+          pw[2] = pw[3] = 0u;
         }
       }
       pb[step] = __builtin_bit_cast(bf16x8, pw);
@@ -403,8 +485,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     // V^T as the A operand through transpose reads, RA units (one MFMA each)
     // ahead of the MFMAs.
     constexpr int NU = NPV * DBLK;
-    constexpr int RA = NU < 4 ? NU : 4;
-    u32x4 vfrag[NU];
+    constexpr int RA_MAX = kPV16 ? 8 : 4;  // transpose reads in flight: at most 8
+    constexpr int RA = NU < RA_MAX ? NU : RA_MAX;
+    // A 16x16x16 operand is one transpose read (u32x2): the read writes the
+    // operand register itself, with no copy that could run ahead of the wait.
+    using VFrag = typename std::conditional<kPV16, u32x2, u32x4>::type;
+    VFrag vfrag[NU];
     auto issue_v = [&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       constexpr int step = U / DBLK, db = U % DBLK;
@@ -412,33 +498,42 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       constexpr uint32_t row_step = (MT == 32) ? 16u * D * 2 : 32u * D * 2;
       constexpr uint32_t col_step = (uint32_t)(db / VPER) * VPER * MT * 2;
       constexpr uint32_t imm1 = stage_bytes + step * row_step + col_step;
-      // (a half-filled 16-key step re-reads its own rows for the zero-P half)
+      // (a half-filled 32-deep step re-reads its own rows for the zero-P half)
       constexpr uint32_t imm2 = imm1 + ((MT == 32 || KT == 16) ? 0u : 16u * D * 2);
       const uint32_t a1 = v_lds + voff[0][db % VPER];
-      const uint32_t a2 = v_lds + voff[VROWS - 1][db % VPER];
-      const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
-      const u32x2 hi = lds_read_tr16_imm<imm2>(a2);
-      vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      if constexpr (kPV16) {
+        vfrag[U] = lds_read_tr16_imm<imm1>(a1);
+      } else {
+        const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
+        const uint32_t a2 = v_lds + voff[VROWS - 1][db % VPER];
+        const u32x2 hi = lds_read_tr16_imm<imm2>(a2);
+        vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
     };
     static_for<0, RA>([&](auto u_c) { issue_v(u_c); });
     static_for<0, NU>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
-      constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
+      constexpr int kReadsPerUnit = kPV16 ? 1 : 2;
+      constexpr int pending = kReadsPerUnit * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
       lds_wait_tied<pending>(vfrag[U]);
-      oacc[U % DBLK] = M::run(__builtin_bit_cast(bf16x8, vfrag[U]), pb[U / DBLK], oacc[U % DBLK]);
+      if constexpr (kPV16) {
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb[0]);
+        oacc[U % DBLK] = mfma16x16x16(__builtin_bit_cast(bf16x4, vfrag[U]),
+                                      __builtin_bit_cast(bf16x4, u32x2{pw[0], pw[1]}),
+                                      oacc[U % DBLK]);
+      } else {
+        oacc[U % DBLK] =
+            M::run(__builtin_bit_cast(bf16x8, vfrag[U]), pb[U / DBLK], oacc[U % DBLK]);
+      }
     });
   };
 
-  for (int it0 = 0; it0 < ntiles; it0 += STAGES) {
-    tile(std::integral_constant<int, 0>{}, it0);
-    if (it0 + 1 < ntiles) tile(std::integral_constant<int, 1>{}, it0 + 1);
-    if constexpr (STAGES > 2) {
-      if (it0 + 2 < ntiles) tile(std::integral_constant<int, 2 % STAGES>{}, it0 + 2);
-    }
-    if constexpr (STAGES > 3) {
-      if (it0 + 3 < ntiles) tile(std::integral_constant<int, 3 % STAGES>{}, it0 + 3);
-    }
+  for (int it0 = 0; it0 < ntiles; it0 += LCM) {
+    static_for<0, LCM>([&](auto u_c) {
+      constexpr int U = decltype(u_c)::value;
+      if (it0 + U < ntiles) tile(u_c, it0 + U);
+    });
   }
 
   // ---- epilogue: O / l, log-sum-exp ----

@@ -65,6 +65,15 @@ template <> struct Mfma<16> {
   }
 };
 
+// v_mfma_f32_16x16x16_bf16: A[16 x 16] * B[16 x 16] -> C[16 x 16]; lane holds
+// A[lane % 16][4*(lane / 16) + e] and B[4*(lane / 16) + e][lane % 16], e = 0..3,
+// C as for 16x16x32.  Used for the PV product of 16-key tiles, whose
+// probabilities already sit in this B layout (keys 4*(lane/16) + r).
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+__device__ inline f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // Row index (within an MT-row block) of accumulator register r in this lane.
 template <int MT> __device__ inline int acc_row(int lane, int r);
 template <> __device__ inline int acc_row<32>(int lane, int r) {
@@ -143,11 +152,38 @@ __device__ inline u32x2 lds_read_tr16_imm(uint32_t lds_addr) {
   return r;
 }
 
+// 16-byte LDS read issued from inline asm, with a constant byte offset
+// folded into the instruction, for the same reason as the transpose reads: a
+// compiler-visible LDS read after asynchronous global->LDS copies makes the
+// compiler wait for every copy in flight (vmcnt(0)) first.
+template <uint32_t OFF>
+__device__ inline u32x4 lds_read_b128_imm(uint32_t lds_addr) {
+  static_assert(OFF < 65536u, "DS offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N) with no register tie; follow it with lds_tie on each
+// result it covers.
+template <int N>
+__device__ inline void lds_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+}
+
+// Marks r as produced here (after a preceding lds_wait), so no use of r can be
+// scheduled before that wait.
+template <typename T>
+__device__ inline void lds_tie(T& r) {
+  asm volatile("" : "+v"(r));
+}
+
 // s_waitcnt lgkmcnt(N) tied to a register tuple, so the compiler cannot use
 // the tuple before the wait.  LDS operations complete in order, so waiting for
 // at most N outstanding means everything issued before the last N is done.
-template <int N>
-__device__ inline void lds_wait_tied(u32x4& r) {
+template <int N, typename T>
+__device__ inline void lds_wait_tied(T& r) {
   static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
 }

@@ -10,20 +10,21 @@
 namespace fmha {
 namespace {
 
-template <int D, int MT, int NW, int KT, int ST, bool C, bool S>
+template <int D, int MT, int NW, int KT, int KS, int VS, bool C, bool S>
 fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, ST, C, S>), grid, dim3(NW * 64), 0, st, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, S>), grid, dim3(NW * 64), 0, st,
+                     p);
   return check_launch("attention kernel launch");
 }
 
-template <int D, int MT, int NW, int KT, int ST>
+template <int D, int MT, int NW, int KT, int KS, int VS>
 fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
                            hipStream_t st) {
   if (causal)
-    return split ? launch_attn<D, MT, NW, KT, ST, true, true>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, ST, true, false>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, ST, false, true>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, ST, false, false>(p, grid, st);
+    return split ? launch_attn<D, MT, NW, KT, KS, VS, true, true>(p, grid, st)
+                 : launch_attn<D, MT, NW, KT, KS, VS, true, false>(p, grid, st);
+  return split ? launch_attn<D, MT, NW, KT, KS, VS, false, true>(p, grid, st)
+               : launch_attn<D, MT, NW, KT, KS, VS, false, false>(p, grid, st);
 }
 
 }  // namespace
@@ -32,10 +33,10 @@ fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool spl
 // a 3-stage LDS ring (2 stages at head dim 128).
 fmha_status launch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
   switch (D) {
-    case 16: return launch_attn_cs<16, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 32: return launch_attn_cs<32, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 64: return launch_attn_cs<64, 32, 4, 64, 3>(p, grid, causal, false, st);
-    case 128: return launch_attn_cs<128, 32, 4, 64, 2>(p, grid, causal, false, st);
+    case 16: return launch_attn_cs<16, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
+    case 32: return launch_attn_cs<32, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
+    case 64: return launch_attn_cs<64, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
+    case 128: return launch_attn_cs<128, 32, 4, 64, 2, 2>(p, grid, causal, false, st);
   }
   return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dim %d not built", D);
 }

@@ -38,11 +38,11 @@ struct DecodeCfg {
 
 // One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
 // small workgroups keep enough loads in flight per CU); four waves otherwise.
-// Head dim 512 always uses four waves sharing a 16-key, 4-stage ring (128 KB,
-// three tiles in flight).
+// Head dim 512: four waves sharing 32-key tiles in a 3-deep K ring and a
+// 2-deep V ring (160 KB of LDS, the whole CU).
 // Must match the instantiations in fmha_decode.hip.
 inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
-  if (D == 512) return {4, 16, 1};
+  if (D == 512) return {4, 32, 1};
   if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 5};
   return {4, 64, D == 64 ? 3 : 2};
 }

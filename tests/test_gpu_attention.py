@@ -125,6 +125,8 @@ DEC_CASES = [
     (2, 8, 2, 1, 1000, 64, False, 0),
     (1, 64, 1, 1, 777, 512, False, 4),
     (1, 64, 1, 1, 300, 512, False, 1),
+    (8, 64, 1, 1, 300, 512, False, 1),
+    (2, 32, 2, 1, 500, 512, False, 3),  # two KV heads of 32 rows
     (3, 4, 4, 1, 513, 128, False, 1),
     (3, 4, 4, 1, 513, 128, False, 5),
     (2, 16, 2, 4, 390, 64, True, 2),    # small Sq > 1, causal bottom-right
