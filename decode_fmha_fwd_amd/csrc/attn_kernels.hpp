@@ -198,9 +198,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
   constexpr int ROWS_WG = NW * MT;
   // PV instructions per d-block: 16 keys each for 32-row waves, 32 keys each
-  // for 16-row waves -- except 16-key tiles, which use the 16x16x16 MFMA.
-  constexpr bool kPV16 = (MT == 16 && KT == 16);
-  constexpr int NPV = (MT == 32) ? 2 * KBLK : (kPV16 ? 1 : (KBLK + 1) / 2);
+  // for 16-row waves (a 16-key tile fills half of one; the other half gets P = 0).
+  constexpr int NPV = (MT == 32) ? 2 * KBLK : (KBLK + 1) / 2;
   constexpr int TILE_ELEMS = KT * D;
   constexpr int kPerTile = 2 * Copy::kLoads;       // copies per wave per tile (K and V)
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
@@ -211,7 +210,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int kMaxPending = (KST == VST) ? (KST - 2) * kPerTile
                                            : Copy::kLoads + (VST - 2) * kPerTile;
   static_assert(kMaxPending < 64, "vmcnt range");
-  static_assert(VST * TILE_ELEMS * 2 <= 65536, "V ring must fit the 16-bit DS offset");
   constexpr int LCM = (KST == VST) ? KST : KST * VST;  // loop unroll: both stages constant
 
   // V ring first in LDS so that every V transpose read can carry its full LDS
@@ -387,7 +385,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         }
       });
     };
+    // With one key block per tile the contraction alternates between two
+    // accumulators, so consecutive MFMAs do not wait on each other's result.
+    constexpr int NCH = (KBLK == 1 && KSTEPS >= 4) ? 2 : 1;
     Acc sacc[KBLK];
+    Acc sacc2{};
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) sacc[kb] = Acc{};
     read_k(std::integral_constant<int, 0>{});
@@ -410,10 +412,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int kb = 0; kb < KBLK; ++kb) {
           const int s = C * QCH + i;
-          if (s < KSTEPS)
-            sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[C][kb][i]), qf[s], sacc[kb]);
+          if (s < KSTEPS) {
+            if (NCH == 2 && (s & 1))
+              sacc2 = M::run(__builtin_bit_cast(bf16x8, kf[C][kb][i]), qf[s], sacc2);
+            else
+              sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[C][kb][i]), qf[s], sacc[kb]);
+          }
         }
     });
+    if constexpr (NCH == 2) sacc[0] += sacc2;
 
     // ---- mask the ragged end and the causal diagonal ----
     const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
@@ -466,10 +473,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         pw[1] = pack_bf16x2(sacc[kb][8 * t2 + 2], sacc[kb][8 * t2 + 3]);
         pw[2] = pack_bf16x2(sacc[kb][8 * t2 + 4], sacc[kb][8 * t2 + 5]);
         pw[3] = pack_bf16x2(sacc[kb][8 * t2 + 6], sacc[kb][8 * t2 + 7]);
-      } else if constexpr (kPV16) {
-        pw[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);  // keys 4g + 0..3 (one 16x16x16)
-        pw[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
-        pw[2] = pw[3] = 0u;
       } else {
         pw[0] = pack_bf16x2(sacc[2 * step][0], sacc[2 * step][1]);
         pw[1] = pack_bf16x2(sacc[2 * step][2], sacc[2 * step][3]);
@@ -485,47 +488,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     // V^T as the A operand through transpose reads, RA units (one MFMA each)
     // ahead of the MFMAs.
     constexpr int NU = NPV * DBLK;
-    constexpr int RA_MAX = kPV16 ? 8 : 4;  // transpose reads in flight: at most 8
-    constexpr int RA = NU < RA_MAX ? NU : RA_MAX;
-    // A 16x16x16 operand is one transpose read (u32x2): the read writes the
-    // operand register itself, with no copy that could run ahead of the wait.
-    using VFrag = typename std::conditional<kPV16, u32x2, u32x4>::type;
-    VFrag vfrag[NU];
+    constexpr int RA = NU < 4 ? NU : 4;
+    constexpr bool kVStageImm = (uint32_t)VST * TILE_ELEMS * 2 <= 65536u;
+    const uint32_t vst = v_lds + (kVStageImm ? 0u : (uint32_t)STG * TILE_ELEMS * 2);
+    u32x4 vfrag[NU];
     auto issue_v = [&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       constexpr int step = U / DBLK, db = U % DBLK;
-      constexpr uint32_t stage_bytes = (uint32_t)STG * TILE_ELEMS * 2;
+      // stage offset: an instruction immediate when the V ring fits the 16-bit
+      // DS offset, else folded into the per-tile base vst
+      constexpr uint32_t stage_bytes = kVStageImm ? (uint32_t)STG * TILE_ELEMS * 2 : 0u;
       constexpr uint32_t row_step = (MT == 32) ? 16u * D * 2 : 32u * D * 2;
       constexpr uint32_t col_step = (uint32_t)(db / VPER) * VPER * MT * 2;
       constexpr uint32_t imm1 = stage_bytes + step * row_step + col_step;
       // (a half-filled 32-deep step re-reads its own rows for the zero-P half)
       constexpr uint32_t imm2 = imm1 + ((MT == 32 || KT == 16) ? 0u : 16u * D * 2);
-      const uint32_t a1 = v_lds + voff[0][db % VPER];
-      if constexpr (kPV16) {
-        vfrag[U] = lds_read_tr16_imm<imm1>(a1);
-      } else {
-        const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
-        const uint32_t a2 = v_lds + voff[VROWS - 1][db % VPER];
-        const u32x2 hi = lds_read_tr16_imm<imm2>(a2);
-        vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
+      const uint32_t a1 = vst + voff[0][db % VPER];
+      const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
+      const uint32_t a2 = vst + voff[VROWS - 1][db % VPER];
+      const u32x2 hi = lds_read_tr16_imm<imm2>(a2);
+      vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
     static_for<0, RA>([&](auto u_c) { issue_v(u_c); });
     static_for<0, NU>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
-      constexpr int kReadsPerUnit = kPV16 ? 1 : 2;
-      constexpr int pending = kReadsPerUnit * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
+      constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
       lds_wait_tied<pending>(vfrag[U]);
-      if constexpr (kPV16) {
-        const u32x4 pw = __builtin_bit_cast(u32x4, pb[0]);
-        oacc[U % DBLK] = mfma16x16x16(__builtin_bit_cast(bf16x4, vfrag[U]),
-                                      __builtin_bit_cast(bf16x4, u32x2{pw[0], pw[1]}),
-                                      oacc[U % DBLK]);
-      } else {
-        oacc[U % DBLK] =
-            M::run(__builtin_bit_cast(bf16x8, vfrag[U]), pb[U / DBLK], oacc[U % DBLK]);
-      }
+      oacc[U % DBLK] =
+          M::run(__builtin_bit_cast(bf16x8, vfrag[U]), pb[U / DBLK], oacc[U % DBLK]);
     });
   };
 

@@ -65,15 +65,6 @@ template <> struct Mfma<16> {
   }
 };
 
-// v_mfma_f32_16x16x16_bf16: A[16 x 16] * B[16 x 16] -> C[16 x 16]; lane holds
-// A[lane % 16][4*(lane / 16) + e] and B[4*(lane / 16) + e][lane % 16], e = 0..3,
-// C as for 16x16x32.  Used for the PV product of 16-key tiles, whose
-// probabilities already sit in this B layout (keys 4*(lane/16) + r).
-typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
-__device__ inline f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 // Row index (within an MT-row block) of accumulator register r in this lane.
 template <int MT> __device__ inline int acc_row(int lane, int r);
 template <> __device__ inline int acc_row<32>(int lane, int r) {
