@@ -95,20 +95,48 @@ __device__ inline float xor_lane(float v, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
 
+// Symmetric exchange across lane halves without the LDS crossbar (gfx950
+// v_permlane{16,32}_swap, lane layout checked on the GPU): with both operands
+// holding v, the swap leaves in every lane its own value and its partner's
+// (lane ^ 16, resp. lane ^ 32), so a commutative op on the pair is the
+// pairwise reduction.
+template <int HALF>
+__device__ inline void swap_halves(float v, float& x, float& y) {
+  const unsigned a = __builtin_bit_cast(unsigned, v);
+  unsigned r0, r1;
+  if constexpr (HALF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  x = __builtin_bit_cast(float, r0);
+  y = __builtin_bit_cast(float, r1);
+}
+template <int HALF>
+__device__ inline float pair_max(float v) {
+  float x, y;
+  swap_halves<HALF>(v, x, y);
+  return fmaxf(x, y);
+}
+template <int HALF>
+__device__ inline float pair_sum(float v) {
+  float x, y;
+  swap_halves<HALF>(v, x, y);
+  return x + y;
+}
+
 // Reductions over the lanes that hold the same query column of an MT-wide
 // MFMA output (lanes that differ only in bits above log2(MT)).
 template <int MT> __device__ inline float group_max(float v);
-template <> __device__ inline float group_max<32>(float v) { return fmaxf(v, xor_lane(v, 32)); }
-template <> __device__ inline float group_max<16>(float v) {
-  v = fmaxf(v, xor_lane(v, 16));
-  return fmaxf(v, xor_lane(v, 32));
-}
+template <> __device__ inline float group_max<32>(float v) { return pair_max<32>(v); }
+template <> __device__ inline float group_max<16>(float v) { return pair_max<32>(pair_max<16>(v)); }
 template <int MT> __device__ inline float group_sum(float v);
-template <> __device__ inline float group_sum<32>(float v) { return v + xor_lane(v, 32); }
-template <> __device__ inline float group_sum<16>(float v) {
-  v += xor_lane(v, 16);
-  return v + xor_lane(v, 32);
-}
+template <> __device__ inline float group_sum<32>(float v) { return pair_sum<32>(v); }
+template <> __device__ inline float group_sum<16>(float v) { return pair_sum<32>(pair_sum<16>(v)); }
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
