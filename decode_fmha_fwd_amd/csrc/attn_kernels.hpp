@@ -609,7 +609,10 @@ __global__ __launch_bounds__(256) void qk_scores_debug_kernel(const uint16_t* q,
 // Log-sum-exp combine of split results: one wave per query row.
 //   m = max_s lse_s;  LSE = m + log sum_s exp(lse_s - m);
 //   O = sum_s exp(lse_s - LSE) * O_s  -> bf16.
-// Splits with lse_s = -inf (no visible key) weigh 0.
+// Splits with lse_s = -inf (no visible key) weigh 0.  The split weights are
+// computed once, one split per lane (64 splits per pass), and broadcast with
+// v_readlane; the partial rows are then read 16 bytes per lane, several
+// splits ahead of the accumulation.
 template <int D>
 __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restrict__ o_part,
                                                           const float* __restrict__ lse_part,
@@ -617,8 +620,10 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
                                                           float* __restrict__ lse,
                                                           float* __restrict__ o_amax,
                                                           long long nrows, int nsplit) {
-  constexpr int VPL = D / 64;  // output elements per lane
   static_assert(D % 64 == 0, "combine expects D a multiple of 64");
+  // lanes that own 4 consecutive outputs each; the rest idle in the sum
+  constexpr int VL = D / 4 < 64 ? D / 4 : 64;   // active lanes
+  constexpr int NV = D / (4 * VL);               // float4 groups per active lane
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= nrows) return;
@@ -629,7 +634,7 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
   m = wave_max(m);
   float amax = 0.0f;
   if (m == -__builtin_inff()) {
-    for (int e = 0; e < VPL; ++e) o[row * D + lane * VPL + e] = 0;
+    for (int e = lane; e < D; e += 64) o[row * D + e] = 0;
     if (lane == 0 && lse) lse[row] = -__builtin_inff();
   } else {
     float sum = 0.0f;
@@ -637,26 +642,51 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) sum += xor_lane(sum, msk);
     const float L = m + __logf(sum);
-    float acc[VPL];
+    f32x4 acc[NV];
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) acc[e] = 0.0f;
-    const float* op = o_part + row * nsplit * D + lane * VPL;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = __expf(lp[s] - L);
+    for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float* op = o_part + row * nsplit * D + 4 * (lane < VL ? lane : 0);  // idle lanes: in bounds
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+      // this lane's split weight, then broadcast split by split
+      const int sl = s0 + lane;
+      const float wl = sl < nsplit ? __expf(lp[sl] - L) : 0.0f;
+      const int n = nsplit - s0 < 64 ? nsplit - s0 : 64;
+      int s = 0;
+      for (; s + 4 <= n; s += 4) {
+        f32x4 x[4][NV];
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) acc[e] += w * op[(long long)s * D + e];
-    }
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int e = 0; e < VPL; e += 2) {
-      const float hi = (e + 1 < VPL) ? acc[e + 1] : 0.0f;
-      const uint32_t w = pack_bf16x2(acc[e], hi);
-      if (VPL >= 2) {
-        *(uint32_t*)(o + row * D + lane * VPL + e) = w;
-      } else {
-        o[row * D + lane * VPL + e] = (uint16_t)(w & 0xFFFF);
+          for (int v = 0; v < NV; ++v)
+            x[u][v] = lane < VL ? *(const f32x4*)(op + (long long)(s0 + s + u) * D + v * 4 * VL)
+                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s + u));
+#pragma unroll
+          for (int v = 0; v < NV; ++v) acc[v] += w * x[u][v];
+        }
       }
-      amax = fmaxf(amax, fabsf(bf16_bits_to_float(w & 0xFFFF)));
-      if (e + 1 < VPL) amax = fmaxf(amax, fabsf(bf16_bits_to_float(w >> 16)));
+      for (; s < n; ++s) {
+        const float w =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane < VL) acc[v] += w * *(const f32x4*)(op + (long long)(s0 + s) * D + v * 4 * VL);
+      }
+    }
+    if (lane < VL) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t w0 = pack_bf16x2(acc[v][0], acc[v][1]);
+        const uint32_t w1 = pack_bf16x2(acc[v][2], acc[v][3]);
+        *(u32x2*)(o + row * D + v * 4 * VL + 4 * lane) = u32x2{w0, w1};
+        amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 >> 16)));
+      }
     }
     if (lane == 0 && lse) lse[row] = L;
   }
