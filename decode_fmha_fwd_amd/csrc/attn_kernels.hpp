@@ -143,11 +143,13 @@ struct TileCopy {
   static_assert(kLoads >= 1 && kLoads * NW * 64 * kBytes == kTileBytes,
                 "tile must split evenly over the workgroup's copies");
 
+  // Copies [J0, J1) of the tile (all of them by default).
+  template <int J0 = 0, int J1 = kLoads>
   __device__ static inline void issue(const uint16_t* base, int stride, int col0, int t0, int Sk,
                                       FMHA_LDS char* lds, int wave, int lane) {
     constexpr int CPR = W / 8;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int slot = (j * NW + wave) * 64 + lane;
       const int byte = slot * kBytes;
       const int row = byte / (W * 2);
@@ -270,12 +272,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
 
-  auto issue_k = [&](int it, int stage) {
-    Copy::issue(kbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
+  auto issue_k = [&](int it, int stage, auto j0_c, auto j1_c) {
+    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+        kbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
   };
-  auto issue_v = [&](int it, int stage) {
-    Copy::issue(vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
+  auto issue_v = [&](int it, int stage, auto j0_c, auto j1_c) {
+    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+        vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
   };
+  using All0 = std::integral_constant<int, 0>;
+  using AllN = std::integral_constant<int, Copy::kLoads>;
   // Copies of this wave issued after both K(it) and V(it) (see the issue
   // order: prologue V0 K0 V1 K1 ..., then per tile V(it+VST-1), K(it+KST-1)).
   auto pending_after = [&](int it) {
@@ -298,8 +304,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   // Prologue: the first tiles in flight before Q is even loaded.
 #pragma unroll
   for (int s = 0; s < KST - 1; ++s) {
-    if (s < VST - 1 && s < ntiles) issue_v(s, s);
-    if (s < ntiles) issue_k(s, s);
+    if (s < VST - 1 && s < ntiles) issue_v(s, s, All0{}, AllN{});
+    if (s < ntiles) issue_k(s, s, All0{}, AllN{});
   }
 
   bf16x8 qf[KSTEPS];
@@ -354,18 +360,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     wait_vmcnt_at_most<kMaxPending>(pending_after(it));
     wait_lgkmcnt0();
     lds_barrier();
-    if (it + VST - 1 < ntiles) issue_v(it + VST - 1, (U + VST - 1) % VST);
-    if (it + KST - 1 < ntiles) issue_k(it + KST - 1, (U + KST - 1) % KST);
+    // Decode spreads the copies for later tiles through this tile's work,
+    // V's over the QK steps and K's over the PV steps (same order and count
+    // as issuing them all here), so the memory pipeline is fed while the wave
+    // computes instead of the wave stalling on one long burst of issues into
+    // a full memory queue.  Prefill (copies from L2) issues them here.
+    constexpr bool kSpread = (MT == 16);
+    const bool more_v = it + VST - 1 < ntiles, more_k = it + KST - 1 < ntiles;
+    const int v_stage = (U + VST - 1) % VST, k_stage = (U + KST - 1) % KST;
+    if constexpr (!kSpread) {
+      if (more_v) issue_v(it + VST - 1, v_stage, All0{}, AllN{});
+      if (more_k) issue_k(it + KST - 1, k_stage, All0{}, AllN{});
+    }
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
-    if (CAUSAL && t0 > wave_max_last) return;
+    if (CAUSAL && t0 > wave_max_last) {
+      if constexpr (kSpread) {
+        if (more_v) issue_v(it + VST - 1, v_stage, All0{}, AllN{});
+        if (more_k) issue_k(it + KST - 1, k_stage, All0{}, AllN{});
+      }
+      return;
+    }
 
     // ---- S^T = K Q^T ----
     // K fragments are read in chunks of QCH contraction steps, one chunk ahead
-    // of the MFMAs that use it (bounded register footprint at large D; one
-    // step at a time for 32-row waves, whose register budget sets how many
-    // waves share a SIMD).
-    constexpr int QCH = (MT == 32) ? 1 : (KSTEPS < 4 ? KSTEPS : 4);
+    // of the MFMAs that use it (bounded register footprint at large D, and
+    // more points at which decode can slot in its copies; one step at a time
+    // for 32-row waves, whose register budget sets how many waves share a
+    // SIMD).
+    constexpr int QCH = (MT == 32) ? 1 : (KSTEPS < 2 ? KSTEPS : 2);
     constexpr int NQC = (KSTEPS + QCH - 1) / QCH;
     // Byte offset of this tile's K stage: an instruction immediate when the
     // whole ring fits the 16-bit DS offset, else added once per tile.
@@ -395,6 +418,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     read_k(std::integral_constant<int, 0>{});
     static_for<0, NQC>([&](auto c_c) {
       constexpr int C = decltype(c_c)::value;
+      if (kSpread && more_v)  // V copies [C*L/NQC, (C+1)*L/NQC)
+        issue_v(it + VST - 1, v_stage, std::integral_constant<int, C * Copy::kLoads / NQC>{},
+                std::integral_constant<int, (C + 1) * Copy::kLoads / NQC>{});
       if constexpr (C + 1 < NQC) read_k(std::integral_constant<int, C + 1>{});
       // chunk C has landed once at most the next chunk's reads are in flight
       constexpr int kNext = (C + 1 < NQC) ? KBLK * ((KSTEPS - (C + 1) * QCH) < QCH
@@ -512,6 +538,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     static_for<0, RA>([&](auto u_c) { issue_v(u_c); });
     static_for<0, NU>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
+      if (kSpread && more_k)  // K copies [U*L/NU, (U+1)*L/NU)
+        issue_k(it + KST - 1, k_stage, std::integral_constant<int, U * Copy::kLoads / NU>{},
+                std::integral_constant<int, (U + 1) * Copy::kLoads / NU>{});
       if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
       constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
       lds_wait_tied<pending>(vfrag[U]);

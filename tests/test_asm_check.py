@@ -5,7 +5,11 @@ from decode_fmha_fwd_amd.asm_check import check_text
 
 
 def _asm(*lines):
-    return "\n".join(["kern:"] + ["\t" + l for l in lines]) + "\n"
+    """A kernel body: entries ending in ':' are block labels (column 0)."""
+    out = ["kern:"]
+    for l in lines:
+        out.append(l if l.endswith(":") else "\t" + l)
+    return "\n".join(out) + "\n"
 
 
 READ = [";;#ASMSTART", "ds_read_b64_tr_b16 v[0:1], v10 offset:64", ";;#ASMEND"]
@@ -45,9 +49,34 @@ def test_write_to_destination_and_scalar_loads():
     assert len(smem.problems) == 1
 
 
-def test_pending_read_at_branch_is_flagged():
-    r = check_text(_asm(*READ, "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)"))
-    assert any("branch" in p for p in r.problems)
+def test_use_on_a_branch_path_before_the_wait_is_flagged():
+    r = check_text(_asm(*READ, "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)",
+                        ".LBB0_2:", "v_mov_b32_e32 v9, v0", "s_waitcnt lgkmcnt(0)"))
+    assert len(r.problems) == 1 and "v_mov_b32_e32 v9, v0" in r.problems[0]
+
+
+def test_wait_on_every_path_after_a_branch_is_fine():
+    # the kernels issue copies under uniform branches while LDS reads are in
+    # flight; every path then reaches the wait before the use
+    r = check_text(_asm(*READ, "s_cbranch_scc0 .LBB0_2", "global_load_lds_dwordx4 v[4:5], off",
+                        ".LBB0_2:", "s_waitcnt lgkmcnt(0)", "v_mov_b32_e32 v9, v0"))
+    assert r.problems == []
+
+
+def test_join_keeps_the_fewest_later_lds_ops():
+    # on the taken path one more LDS op follows the read; on the other none, so
+    # lgkmcnt(1) at the join does not cover the read
+    r = check_text(_asm(*READ, "s_cbranch_scc0 .LBB0_2", "ds_read_b32 v20, v21",
+                        ".LBB0_2:", "s_waitcnt lgkmcnt(1)", "v_mov_b32_e32 v9, v0",
+                        "s_waitcnt lgkmcnt(0)"))
+    assert len(r.problems) == 1
+
+
+def test_read_pending_around_a_loop_is_flagged():
+    # a read issued at the bottom of a loop and used at its top without a wait
+    r = check_text(_asm(".LBB0_1:", "v_mov_b32_e32 v9, v0", *READ, "s_cbranch_scc1 .LBB0_1",
+                        "s_waitcnt lgkmcnt(0)"))
+    assert len(r.problems) == 1
 
 
 def test_compiler_managed_reads_are_not_tracked():
