@@ -133,6 +133,8 @@ DEC_CASES = [
     (2, 32, 1, 2, 129, 128, False, 2),  # 64 rows per KV head, 4 waves
     (1, 4, 1, 1, 1, 64, False, 1),      # one key
     (1, 2, 1, 1, 40, 64, False, 8),     # more splits than tiles: empty ranges
+    (1, 4, 1, 1, 2400, 64, False, 75),  # more than 64 splits: the combine's second pass
+    (1, 64, 1, 1, 4200, 512, False, 70),  # 66 effective splits at head dim 512
 ]
 
 
