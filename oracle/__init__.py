@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
         L.oracle_e2m1_encode.restype = ctypes.c_uint8
         L.oracle_nvfp4_quantize.argtypes = [P, i64, i32, P, P, P]
+        L.oracle_nvfp4_quantize_with_scale.argtypes = [P, i64, i32, ctypes.c_float, P, P]
         L.oracle_double_to_bf16_array.argtypes = [P, i64, P]
         L.oracle_bf16_to_double_array.argtypes = [P, i64, P]
         L.oracle_e4m3_encode_array.argtypes = [P, i64, P]
@@ -71,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = i32
         for f in ("oracle_attention", "oracle_attention_splits", "oracle_combine",
-                  "oracle_nvfp4_quantize"):
+                  "oracle_nvfp4_quantize", "oracle_nvfp4_quantize_with_scale"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -192,6 +193,20 @@ def nvfp4_quantize(x_bits, rows, cols):
     if rc:
         raise ValueError(f"oracle_nvfp4_quantize failed with code {rc}")
     return codes, scales, g[0]
+
+
+def nvfp4_quantize_with_scale(x_bits, rows, cols, g):
+    """O3 per-block recipe for a given global scale g (float32).  Returns
+    (codes[rows, cols/2] u8, scales[rows, cols/16] u8)."""
+    xa = _u16(x_bits)
+    assert xa.size == rows * cols
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    rc = lib().oracle_nvfp4_quantize_with_scale(_ptr(xa), rows, cols, float(np.float32(g)),
+                                                _ptr(codes), _ptr(scales))
+    if rc:
+        raise ValueError(f"oracle_nvfp4_quantize_with_scale failed with code {rc}")
+    return codes, scales
 
 
 def num_threads() -> int:

@@ -307,28 +307,22 @@ uint8_t oracle_e2m1_encode(float q)
     return sign | (uint8_t)best;
 }
 
-/* Quantise a bf16 matrix x[rows, cols] (cols % 16 == 0) to NVFP4:
- *   amax = max |x| over the whole tensor; g = amax / 2688 (2688 = 6*448);
- *   per 16-element block along a row: s = E4M3((amax_b / 6) / g),
- *   t = value(s) * g, and for each element code = E2M1(x / t);
+/* The per-block part of the NVFP4 recipe for a given global scale g: per
+ * 16-element block along a row of the bf16 matrix x[rows, cols]
+ * (cols % 16 == 0): s = E4M3((amax_b / 6) / g), t = value(s) * g, and for
+ * each element code = E2M1(x / t);
  *   codes[r, c/2] = code[c+1] << 4 | code[c]   (low nibble = even element),
- *   scales[r, c/16] = s, *gscale = g.
- * Degenerate cases: amax == 0 (or g underflowing to 0) gives g = 0 and all
- * scales and codes 0; a block with s == 0, or with t underflowing to 0, gets
- * all codes 0.  Every arithmetic step is one correctly rounded binary32
- * operation. */
-int oracle_nvfp4_quantize(const uint16_t *x, long long rows, int cols,
-                          uint8_t *codes, uint8_t *scales, float *gscale)
+ *   scales[r, c/16] = s.
+ * g <= 0 gives all scales and codes 0; a block with s == 0, or with t
+ * underflowing to 0, gets all codes 0.  Every arithmetic step is one
+ * correctly rounded binary32 operation.  (The tensor-wide recipe below uses
+ * g = amax / 2688; a caller that already holds g, e.g. from an earlier step,
+ * quantises with it directly.) */
+int oracle_nvfp4_quantize_with_scale(const uint16_t *x, long long rows, int cols, float g,
+                                     uint8_t *codes, uint8_t *scales)
 {
-    if (!x || !codes || !scales || !gscale) return 1;
+    if (!x || !codes || !scales) return 1;
     if (rows < 0 || cols < 16 || cols % 16) return 2;
-    float amax = 0.0f;
-    for (long long i = 0; i < rows * cols; ++i) {
-        float a = fabsf((float)oracle_bf16_to_double(x[i]));
-        if (a > amax) amax = a;
-    }
-    volatile float g = amax / 2688.0f;
-    *gscale = g;
     int nb = cols / 16;
     for (long long r = 0; r < rows; ++r) {
         for (int b = 0; b < nb; ++b) {
@@ -361,6 +355,25 @@ int oracle_nvfp4_quantize(const uint16_t *x, long long rows, int cols,
         }
     }
     return 0;
+}
+
+/* Quantise a bf16 matrix x[rows, cols] (cols % 16 == 0) to NVFP4:
+ *   amax = max |x| over the whole tensor; g = amax / 2688 (2688 = 6*448);
+ *   then the per-block recipe above with that g; *gscale = g.
+ * amax == 0 (or g underflowing to 0) gives g = 0 and all scales and codes 0. */
+int oracle_nvfp4_quantize(const uint16_t *x, long long rows, int cols,
+                          uint8_t *codes, uint8_t *scales, float *gscale)
+{
+    if (!x || !codes || !scales || !gscale) return 1;
+    if (rows < 0 || cols < 16 || cols % 16) return 2;
+    float amax = 0.0f;
+    for (long long i = 0; i < rows * cols; ++i) {
+        float a = fabsf((float)oracle_bf16_to_double(x[i]));
+        if (a > amax) amax = a;
+    }
+    volatile float g = amax / 2688.0f;
+    *gscale = g;
+    return oracle_nvfp4_quantize_with_scale(x, rows, cols, g, codes, scales);
 }
 
 /* ------------------------------------------------------------------ */

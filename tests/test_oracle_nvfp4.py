@@ -205,3 +205,45 @@ def test_planted_mistake_is_caught():
     swapped = ((codes & 0xF) << 4) | (codes >> 4)
     want = np.array([[int(h, 16) for h in row] for row in ex["expected_codes_hex"]], np.uint8)
     assert not np.array_equal(swapped, want)
+
+
+# ------------------------------------------------- given global scale (fused)
+
+def test_given_scale_hand_worked_blocks():
+    """g = 0.5, worked by hand from the format definitions.
+    Block 0: amax 6 -> s = E4M3((6/6)/0.5) = E4M3(2) = 0x40 (exponent 1 + bias 7,
+    mantissa 0); t = 2 * 0.5 = 1, so the codes are E2M1(x) itself:
+    1 -> 2, -2 -> 0xC, 3 -> 5, 0.25 -> 0 (tie between 0 and 0.5: even code),
+    0.5 -> 1, 6 -> 7, -6 -> 0xF, 1.5 -> 3.
+    Block 1: amax 0.75 -> (0.75/6)/0.5 = 0.25 = E4M3 0x28 (exponent -2 + 7);
+    t = 0.125: 0.75 -> 6 -> 7, 0.375 -> 3 -> 5, -0.1875 -> -1.5 -> 0xB."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :8] = [1.0, -2.0, 3.0, 0.25, 0.5, 6.0, -6.0, 1.5]
+    x[0, 16:19] = [0.75, 0.375, -0.1875]
+    bits = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales = oracle.nvfp4_quantize_with_scale(bits, 1, 32, 0.5)
+    np.testing.assert_array_equal(scales, np.array([[0x40, 0x28]], np.uint8))
+    want = [0xC2, 0x05, 0x71, 0x3F, 0, 0, 0, 0, 0x57, 0x0B, 0, 0, 0, 0, 0, 0]
+    np.testing.assert_array_equal(codes, np.array([want], np.uint8))
+
+
+def test_given_scale_saturation_and_zero():
+    x = torch.full((1, 16), 3.0, dtype=torch.bfloat16)
+    # (3/6)/g >= 448 saturates the block scale to 0x7E = 448; t = 448 g and
+    # every x / t = 3 / (448 * 2^-12) ... = 27.4 saturates E2M1 to 6 (code 7)
+    codes, scales = oracle.nvfp4_quantize_with_scale(x, 1, 16, 2.0 ** -12)
+    assert (scales == 0x7E).all() and (codes == 0x77).all()
+    codes, scales = oracle.nvfp4_quantize_with_scale(x, 1, 16, 0.0)
+    assert not scales.any() and not codes.any()
+
+
+def test_given_scale_with_the_tensor_scale_is_the_tensor_recipe():
+    rows, cols = 16, 64
+    q, _, _ = make_qkv(1, 1, 1, rows, 1, cols, seed=7)
+    x = q.reshape(rows, cols)
+    codes, scales, g = oracle.nvfp4_quantize(x, rows, cols)
+    amax = np.float32(np.abs(x.float().numpy()).max())
+    assert g == np.float32(amax / np.float32(2688.0))
+    c2, s2 = oracle.nvfp4_quantize_with_scale(x, rows, cols, g)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, scales)
