@@ -34,6 +34,8 @@ SIGNATURES = {
     "fmha_decode_splitkv_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "fmha_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _SZ,
                                  _P, _P]),
+    "fmha_decode_splitkv_nvfp4": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
+                                       _SZ, _P, _P, _P, _P]),
     "fmha_decode_default_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "nvfp4_quantize_workspace_size": (_SZ, [_LL, _I]),
     "nvfp4_quantize": (_I, [_P, _LL, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -116,6 +118,18 @@ def fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, n
            lib.fmha_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq,
                                    Sk, D, float(scale), int(causal), int(num_splits),
                                    _ptr(workspace), int(workspace_bytes), _ptr(o_amax), st))
+
+
+def fmha_decode_splitkv_nvfp4(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+                              workspace, workspace_bytes, global_scale, codes, scales,
+                              stream=None):
+    lib = load_library()
+    st = stream if stream is not None else _stream(q.device)
+    _check("fmha_decode_splitkv_nvfp4",
+           lib.fmha_decode_splitkv_nvfp4(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                         Hkv, Sq, Sk, D, float(scale), int(causal),
+                                         int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                         _ptr(global_scale), _ptr(codes), _ptr(scales), st))
 
 
 def nvfp4_quantize_workspace_size(rows, cols) -> int:

@@ -41,6 +41,9 @@ PER_FILE = {
     # prefill keeps MFMA accumulators in ordinary VGPRs (no AGPR round trips
     # around the softmax); decode at head dim 512 needs the AGPR file for O
     "fmha_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the decode epilogues can encode NVFP4: the same fp32 semantics as nvfp4.hip
+    "fmha_decode.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt",
+                        "-fno-gpu-flush-denormals-to-zero"],
     "nvfp4.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                   "-fno-gpu-flush-denormals-to-zero"],
 }

@@ -42,6 +42,7 @@
 
 #include "fmha_device.hpp"
 #include "launch.hpp"
+#include "nvfp4_device.hpp"
 
 namespace fmha {
 
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
           *(f32x4*)dst = f32x4{o0, o1, o2, o3};
         } else {
           const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
-          *(u32x2*)(p.o + (row_base + my_r) * D + d0) = u32x2{w0, w1};
+          if (p.o) *(u32x2*)(p.o + (row_base + my_r) * D + d0) = u32x2{w0, w1};
           if (p.o_amax) {
             amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
             amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
@@ -599,6 +600,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     if (p.o_amax) {
       amax = wave_max(amax);
       if (lane == 0) atomic_max_nonneg(p.o_amax, amax);
+    }
+  }
+
+  // Fused NVFP4 output (16-row waves): the 16-element block of head dims
+  // [16 db, 16 db + 16) of this lane's row is spread over the four lanes kg
+  // = 0..3 (4 values each), so its max |x| is a reduction over those lanes.
+  // The values quantised are O rounded to bf16, exactly what the standalone
+  // quantiser would read back.  All lanes take part in the reductions.
+  if constexpr (!SPLIT && MT == 16) {
+    if (p.fp4_codes) {
+      const float g = *p.fp4_gscale;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const uint32_t w0 = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+        const uint32_t w1 = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+        const float x0 = bf16_bits_to_float(w0 & 0xFFFFu), x1 = bf16_bits_to_float(w0 >> 16);
+        const float x2 = bf16_bits_to_float(w1 & 0xFFFFu), x3 = bf16_bits_to_float(w1 >> 16);
+        const float ab =
+            group_max<16>(fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+        float t;
+        const uint32_t sc = nvfp4_block_scale(ab, g, t);
+        const uint32_t c = nvfp4_code(x0, sc, t) | (nvfp4_code(x1, sc, t) << 4) |
+                           (nvfp4_code(x2, sc, t) << 8) | (nvfp4_code(x3, sc, t) << 12);
+        if (row_ok) {
+          const long long r = row_base + my_r;
+          *(uint16_t*)(p.fp4_codes + r * (D / 2) + db * 8 + 2 * kg) = (uint16_t)c;
+          if (kg == 0) p.fp4_scales[r * (D / 16) + db] = (uint8_t)sc;
+        }
+      }
     }
   }
 }
@@ -648,6 +678,9 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
                                                           uint16_t* __restrict__ o,
                                                           float* __restrict__ lse,
                                                           float* __restrict__ o_amax,
+                                                          uint8_t* __restrict__ fp4_codes,
+                                                          uint8_t* __restrict__ fp4_scales,
+                                                          const float* __restrict__ fp4_gscale,
                                                           long long nrows, int nsplit) {
   static_assert(D % 64 == 0, "combine expects D a multiple of 64");
   // lanes that own 4 consecutive outputs each; the rest idle in the sum
@@ -663,7 +696,12 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
   m = wave_max(m);
   float amax = 0.0f;
   if (m == -__builtin_inff()) {
-    for (int e = lane; e < D; e += 64) o[row * D + e] = 0;
+    if (o)
+      for (int e = lane; e < D; e += 64) o[row * D + e] = 0;
+    if (fp4_codes) {
+      for (int e = lane; e < D / 2; e += 64) fp4_codes[row * (D / 2) + e] = 0;
+      for (int e = lane; e < D / 16; e += 64) fp4_scales[row * (D / 16) + e] = 0;
+    }
     if (lane == 0 && lse) lse[row] = -__builtin_inff();
   } else {
     float sum = 0.0f;
@@ -710,7 +748,7 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
       for (int v = 0; v < NV; ++v) {
         const uint32_t w0 = pack_bf16x2(acc[v][0], acc[v][1]);
         const uint32_t w1 = pack_bf16x2(acc[v][2], acc[v][3]);
-        *(u32x2*)(o + row * D + v * 4 * VL + 4 * lane) = u32x2{w0, w1};
+        if (o) *(u32x2*)(o + row * D + v * 4 * VL + 4 * lane) = u32x2{w0, w1};
         amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
         amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
         amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
@@ -718,6 +756,30 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(const float* __restric
       }
     }
     if (lane == 0 && lse) lse[row] = L;
+    // Fused NVFP4 output: a 16-element block is 4 consecutive lanes here (4
+    // values each); every lane takes part in the reduction, idle lanes with 0.
+    if (fp4_codes) {
+      const float g = *fp4_gscale;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t w0 = pack_bf16x2(acc[v][0], acc[v][1]);
+        const uint32_t w1 = pack_bf16x2(acc[v][2], acc[v][3]);
+        const float x0 = bf16_bits_to_float(w0 & 0xFFFFu), x1 = bf16_bits_to_float(w0 >> 16);
+        const float x2 = bf16_bits_to_float(w1 & 0xFFFFu), x3 = bf16_bits_to_float(w1 >> 16);
+        float ab = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+        ab = fmaxf(ab, xor_lane(ab, 1));
+        ab = fmaxf(ab, xor_lane(ab, 2));
+        float t;
+        const uint32_t sc = nvfp4_block_scale(ab, g, t);
+        const uint32_t c = nvfp4_code(x0, sc, t) | (nvfp4_code(x1, sc, t) << 4) |
+                           (nvfp4_code(x2, sc, t) << 8) | (nvfp4_code(x3, sc, t) << 12);
+        if (lane < VL) {
+          const int d0 = v * 4 * VL + 4 * lane;
+          *(uint16_t*)(fp4_codes + row * (D / 2) + d0 / 2) = (uint16_t)c;
+          if ((lane & 3) == 0) fp4_scales[row * (D / 16) + d0 / 16] = (uint8_t)sc;
+        }
+      }
+    }
   }
   if (o_amax) {
     amax = wave_max(amax);

@@ -167,12 +167,21 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
          round_up(rows * ns * sizeof(float), kAlign);
 }
 
-fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
-                                int causal, int num_splits, void* workspace,
-                                size_t workspace_bytes, float* o_amax, void* stream) {
-  g_last_error[0] = 0;
-  fmha_status s = check_common(q, k, v, o, B, Hq, Hkv, Sq, Sk, scale, causal);
+}  // extern "C"
+
+namespace {
+
+// Split-KV decode; with fp4_codes set, the output epilogue (attention kernel
+// without splits, combine kernel with) also writes the NVFP4 encoding of O
+// for the caller's global scale, and o may be null.
+fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                        int num_splits, void* workspace, size_t workspace_bytes, float* o_amax,
+                        uint8_t* fp4_codes, uint8_t* fp4_scales, const float* fp4_gscale,
+                        void* stream) {
+  // o is optional only for the fused NVFP4 output; q stands in for its checks
+  fmha_status s = check_common(q, k, v, (o || !fp4_codes) ? o : q, B, Hq, Hkv, Sq, Sk, scale,
+                               causal);
   if (s != FMHA_OK) return s;
   if (lse && !aligned16(lse)) return fail(FMHA_ERR_ALIGN, "lse must be 16-byte aligned");
   if (o_amax && ((uintptr_t)o_amax & 3)) return fail(FMHA_ERR_ALIGN, "o_amax must be 4-byte aligned");
@@ -195,6 +204,9 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   p.o = (uint16_t*)o;
   p.lse = lse;
   p.o_amax = o_amax;
+  p.fp4_codes = fp4_codes;
+  p.fp4_scales = fp4_scales;
+  p.fp4_gscale = fp4_gscale;
   p.B = B;
   p.Hkv = Hkv;
   p.Sq = Sq;
@@ -223,8 +235,35 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   dim3 grid((unsigned)p.n_row_blocks * ns_eff * Hkv * B);
   s = launch_decode(D, c, p, grid, causal != 0, true, st);
   if (s != FMHA_OK) return s;
-  return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, (long long)rows,
-                          ns_eff, st);
+  return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
+                        fp4_scales, fp4_gscale, (long long)rows, ns_eff, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                                int causal, int num_splits, void* workspace,
+                                size_t workspace_bytes, float* o_amax, void* stream) {
+  g_last_error[0] = 0;
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+                     workspace, workspace_bytes, o_amax, nullptr, nullptr, nullptr, stream);
+}
+
+fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                      float scale, int causal, int num_splits, void* workspace,
+                                      size_t workspace_bytes, const float* global_scale,
+                                      uint8_t* codes, uint8_t* scales, void* stream) {
+  g_last_error[0] = 0;
+  if (!global_scale || !codes || !scales)
+    return fail(FMHA_ERR_NULL, "global_scale, codes and scales must be non-null");
+  if (((uintptr_t)codes & 7u) || ((uintptr_t)global_scale & 3u))
+    return fail(FMHA_ERR_ALIGN, "codes must be 8-byte aligned and global_scale 4-byte");
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+                     workspace, workspace_bytes, nullptr, codes, scales, global_scale, stream);
 }
 
 fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,

@@ -39,21 +39,22 @@ fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bo
 }
 
 fmha_status launch_combine(int D, const float* op, const float* lp, uint16_t* o, float* lse,
-                           float* amax, long long nrows, int nsplit, hipStream_t st) {
+                           float* amax, uint8_t* codes, uint8_t* scales, const float* gscale,
+                           long long nrows, int nsplit, hipStream_t st) {
   const int rows_per_block = 4;
   dim3 grid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
   switch (D) {
     case 64:
       hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
+                         codes, scales, gscale, nrows, nsplit);
       break;
     case 128:
       hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
+                         codes, scales, gscale, nrows, nsplit);
       break;
     case 512:
       hipLaunchKernelGGL(lse_combine_kernel<512>, grid, dim3(256), 0, st, op, lp, o, lse, amax,
-                         nrows, nsplit);
+                         codes, scales, gscale, nrows, nsplit);
       break;
     default:
       return fail(FMHA_ERR_HEAD_DIM, "combine: head dim %d not built", D);

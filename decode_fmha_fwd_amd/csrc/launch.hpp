@@ -18,6 +18,9 @@ struct AttnParams {
   float* o_part;        // fp32 [rows][nsplit][D] (split)
   float* lse_part;      // fp32 [rows][nsplit]   (split)
   float* o_amax;        // optional running max |O| (no split)
+  uint8_t* fp4_codes;   // optional fused NVFP4 output: codes [rows][D/2] (no split)
+  uint8_t* fp4_scales;  //   E4M3 block scales [rows][D/16]
+  const float* fp4_gscale;  //   the caller's global scale (1 float, device)
   int B;
   int Hkv;
   int Sq;
@@ -56,7 +59,8 @@ fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_o
 fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                           bool split, hipStream_t st);
 fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,
-                           float* lse, float* o_amax, long long nrows, int nsplit,
+                           float* lse, float* o_amax, uint8_t* fp4_codes, uint8_t* fp4_scales,
+                           const float* fp4_gscale, long long nrows, int nsplit,
                            hipStream_t st);
 
 }  // namespace fmha

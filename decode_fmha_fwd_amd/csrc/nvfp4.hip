@@ -6,53 +6,19 @@
 // fp32 division and fp32 denormals kept, because every step decides integer
 // codes: each arithmetic operation below is one IEEE binary32 operation.
 //
-// Codecs are written from the format definitions (OCP 8-bit Floating Point
-// Specification, E4M3FN; OCP Microscaling Formats v1.0, E2M1), with
-// round-to-nearest-even:
-//   * E4M3: below 2^-6 the grid is m * 2^-9 (m = 0..7), so the code is
-//     rint(x * 2^9); above, the float's 23-bit mantissa is rounded to 3 bits
-//     (round half to even on the dropped 20 bits, carries run into the
-//     exponent) and the exponent is re-biased from 127 to 7.  x >= 448
-//     saturates to 0x7E.
-//   * E2M1: the magnitude grid {0, .5, 1, 1.5, 2, 3, 4, 6} split at its
-//     midpoints; at a midpoint the even code wins, which decides whether the
-//     comparison is strict.
+// The block codecs live in nvfp4_device.hpp (shared with the fused decode
+// epilogue).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "../../include/fmha.h"
 #include "fmha_device.hpp"
+#include "nvfp4_device.hpp"
 #include "host_common.hpp"
 
 namespace fmha {
 namespace {
-
-__device__ inline uint32_t e4m3_encode(float x) {
-  if (!(x > 0.0f)) return 0u;
-  if (x >= 448.0f) return 0x7Eu;
-  if (x < 0.015625f) {  // 2^-6: subnormal grid m * 2^-9 (m = 8 is the first normal)
-    return (uint32_t)__builtin_rintf(x * 512.0f);
-  }
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // 8-bit exp, 3-bit mantissa
-  const uint32_t c = r - ((127u - 7u) << 3);
-  return c > 0x7Eu ? 0x7Eu : c;
-}
-
-__device__ inline float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
-  return __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));
-}
-
-__device__ inline uint32_t e2m1_encode(float q) {
-  const float a = fabsf(q);
-  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-  return mag | ((__builtin_bit_cast(uint32_t, q) >> 28) & 8u);
-}
 
 __global__ void zero_f32_kernel(float* p) { *p = 0.0f; }
 
@@ -99,22 +65,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   float ab = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) ab = fmaxf(ab, fabsf(xs[e]));
-  uint32_t s = 0;
-  float t = 0.0f;
-  if (g > 0.0f) {
-    const float sixth = ab / 6.0f;
-    const float sf = sixth / g;
-    s = e4m3_encode(sf);
-    t = e4m3_value(s) * g;
-  }
+  float t;
+  const uint32_t s = nvfp4_block_scale(ab, g, t);
   scales[blk] = (uint8_t)s;
   uint32_t lo = 0, hi = 0;
-  if (s != 0 && t > 0.0f) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lo |= e2m1_encode(xs[e] / t) << (4 * e);
+  for (int e = 0; e < 8; ++e) lo |= nvfp4_code(xs[e], s, t) << (4 * e);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hi |= e2m1_encode(xs[8 + e] / t) << (4 * e);
-  }
+  for (int e = 0; e < 8; ++e) hi |= nvfp4_code(xs[8 + e], s, t) << (4 * e);
   *(u32x2*)(codes + blk * 8) = u32x2{lo, hi};
 }
 

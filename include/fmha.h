@@ -92,7 +92,8 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  * combines them:  LSE = m + log sum_s exp(lse_s - m),  m = max_s lse_s,
  * O = sum_s exp(lse_s - LSE) * O_s.   With one split the first kernel writes
  * O and LSE directly and no workspace is used.
- *   D in {64, 128, 512}; Sq*Hq/Hkv <= 64 rows per KV head.
+ *   D in {64, 128, 512}; the Sq*Hq/Hkv rows of a KV head are taken in
+ *   blocks of 16 or 64 (one workgroup each).
  *   num_splits: 0 = heuristic, otherwise 1..1024.
  *   workspace / workspace_bytes: device buffer of at least
  *     fmha_decode_splitkv_workspace_size(...) bytes (may be NULL when that is 0).
@@ -136,6 +137,27 @@ size_t nvfp4_quantize_workspace_size(long long rows, int cols);
 fmha_status nvfp4_quantize(const void* x, long long rows, int cols, uint8_t* codes,
                            uint8_t* scales, float* global_scale, const float* amax_in,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split-KV decode with the NVFP4 quantisation fused into its output epilogue,
+ * for callers that already hold the global scale g (e.g. from a previous step
+ * or a calibration pass), so no tensor-wide amax pass is needed: the "FP4
+ * quantization" item of the feature list done inside the kernel.  Everything
+ * else is as fmha_decode_splitkv.  The values quantised are O rounded to bf16,
+ * so codes and scales equal nvfp4_quantize of that O with this g; the per-block
+ * recipe (s, t, codes, packing, zero cases) is nvfp4_quantize's with
+ * g = *global_scale instead of amax / 2688.  The epilogue that produces the
+ * final O does the encoding: the attention kernel without splits, the combine
+ * kernel with them.
+ *   o: bf16 [B, Hq, Sq, D] output, or NULL to skip writing it.
+ *   global_scale: device fp32 (read, not written).
+ *   codes: [B*Hq*Sq, D/2] bytes, 8-byte aligned; scales: [B*Hq*Sq, D/16] bytes.
+ */
+fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                      float scale, int causal, int num_splits, void* workspace,
+                                      size_t workspace_bytes, const float* global_scale,
+                                      uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
  * Test hook: the raw score tile S = scale * Q K^T of the first (batch, head),

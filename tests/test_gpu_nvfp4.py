@@ -113,3 +113,73 @@ def test_decode_then_quantise_pipeline():
     rc, rs, rg = oracle.nvfp4_quantize(bits(o), o.numel() // 128, 128)
     np.testing.assert_array_equal(c1.cpu().numpy(), rc)
     np.testing.assert_array_equal(s1.cpu().numpy(), rs)
+
+
+# ------------------------------------------- decode with the fused NVFP4 epilogue
+
+def _decode_plain(q, k, v, scale, ns):
+    dev = require_gpu()
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    nb = F.fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    F.fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, False, ns, ws, nb)
+    return o, lse
+
+
+def _decode_fused(q, k, v, scale, ns, g, want_o):
+    dev = require_gpu()
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    rows = B * Hq * Sq
+    o = torch.full_like(q, float("nan")) if want_o else None
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    codes = torch.full((rows, D // 2), 0xAA, dtype=torch.uint8, device=dev)
+    scales = torch.full((rows, D // 16), 0xAA, dtype=torch.uint8, device=dev)
+    nb = F.fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    gd = torch.tensor([g], dtype=torch.float32, device=dev)
+    F.fmha_decode_splitkv_nvfp4(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, False, ns, ws, nb,
+                                gd, codes, scales)
+    torch.cuda.synchronize()
+    return o, lse, codes.cpu().numpy(), scales.cpu().numpy()
+
+
+FUSED_CASES = [
+    # B, Hq, Hkv, Sk, D, num_splits  (Sq = 1)
+    (2, 4, 4, 300, 128, 1),      # no split: the attention kernel's epilogue encodes
+    (2, 8, 2, 1000, 64, 5),      # split: the combine kernel encodes
+    (1, 64, 1, 700, 512, 3),
+    (3, 16, 16, 257, 128, 2),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+@pytest.mark.parametrize("g_mode", ["tensor", "fixed"])
+def test_fused_nvfp4_epilogue_bit_exact(case, g_mode):
+    """Codes and scales of the fused epilogue equal the oracle's per-block
+    recipe applied to the decode's own bf16 output with the same global scale
+    (the output and LSE are unchanged by the fusion)."""
+    B, Hq, Hkv, Sk, D, ns = case
+    dev = require_gpu()
+    q, k, v = (t.to(dev) for t in make_qkv(B, Hq, Hkv, 1, Sk, D, seed=sum(case), sigma=0.8))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    o_ref, lse_ref = _decode_plain(q, k, v, scale, ns)
+    torch.cuda.synchronize()
+    rows = B * Hq
+    o_bits = bits(o_ref.cpu()).reshape(rows, D)
+    if g_mode == "tensor":
+        amax = np.float32(np.abs(o_ref.float().cpu().numpy()).max())
+        g = np.float32(amax / np.float32(2688.0))
+    else:
+        g = np.float32(0.0007)
+    want_c, want_s = oracle.nvfp4_quantize_with_scale(o_bits, rows, D, g)
+    for want_o in (True, False):
+        o, lse, c, s = _decode_fused(q, k, v, scale, ns, float(g), want_o)
+        np.testing.assert_array_equal(s, want_s)
+        np.testing.assert_array_equal(c, want_c)
+        assert torch.equal(lse, lse_ref)
+        if want_o:
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
