@@ -69,13 +69,24 @@ class Runner:
                                                                  w.num_splits)
             if self.ws_bytes:
                 self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
-        if w.kind == "decode_nvfp4":
+        if w.kind in ("decode_nvfp4", "decode_nvfp4_fused"):
             rows = w.B * w.Hq * w.Sq
             self.rows = rows
             self.amax = torch.zeros(1, dtype=torch.float32, device=dev)
             self.codes = torch.empty((rows, w.Dv // 2), dtype=torch.uint8, device=dev)
             self.scales = torch.empty((rows, w.Dv // 16), dtype=torch.uint8, device=dev)
             self.gscale = torch.empty(1, dtype=torch.float32, device=dev)
+        if w.kind == "decode_nvfp4_fused":
+            # the global scale a serving loop would carry over from an earlier
+            # step: here the amax / 2688 of this input's own output
+            o = torch.empty_like(self.q)
+            amax = torch.zeros(1, dtype=torch.float32, device=dev)
+            F.fmha_decode_splitkv(self.q, self.k, self.v, o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
+                                  w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws,
+                                  self.ws_bytes, amax)
+            F.nvfp4_quantize(o, self.rows, w.Dv, self.codes, self.scales, self.gscale, amax,
+                             None, 0)
+            del o
 
     def step(self):
         w, F = self.w, self.F
@@ -85,6 +96,11 @@ class Runner:
         elif w.kind == "decode":
             F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
                                   w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws, self.ws_bytes)
+        elif w.kind == "decode_nvfp4_fused":
+            F.fmha_decode_splitkv_nvfp4(self.q, self.k, self.v, None, self.lse, w.B, w.Hq, w.Hkv,
+                                        w.Sq, w.Sk, w.D, w.scale, w.causal, w.num_splits,
+                                        self.ws, self.ws_bytes, self.gscale, self.codes,
+                                        self.scales)
         else:
             self.amax.zero_()
             F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,

@@ -21,7 +21,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4"
+    kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4", "decode_nvfp4_fused"
     B: int
     Hq: int
     Hkv: int
@@ -63,6 +63,8 @@ class Workload:
         n = 2 * (q + kv + o) + 4 * self.B * self.Hq * self.Sq
         if self.kind == "decode_nvfp4":
             n += o // 2 + o // 16 + 4
+        elif self.kind == "decode_nvfp4_fused":  # codes and scales instead of O; g read
+            n += o // 2 + o // 16 + 4 - 2 * o
         return n
 
     def kv_bytes(self) -> int:
@@ -87,6 +89,10 @@ WORKLOADS = {
                  note="all 64 query heads share one KV head, head dim 512"),
         Workload("decode_nvfp4_d128", "decode_nvfp4", 128, 16, 16, 1, 4096, 128, 128, 1.0, 4,
                  False, num_splits=1, note="MHA decode, O quantised to NVFP4"),
+        Workload("decode_nvfp4_d128_fused", "decode_nvfp4_fused", 128, 16, 16, 1, 4096, 128, 128,
+                 1.0, 4, False, num_splits=1,
+                 note="the same decode with NVFP4 encoded in its epilogue for a global scale "
+                      "held from an earlier step; no bf16 O written"),
     ]
 }
 
