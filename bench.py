@@ -58,7 +58,8 @@ class Runner:
 
         self.w, self.F, self.torch = w, F, torch
         q, k, v = make_workload_inputs(w)
-        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.q, self.k = q.to(dev), k.to(dev)
+        self.v = self.k if w.v_is_k else v.to(dev)  # one buffer when V is K
         del q, k, v
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)

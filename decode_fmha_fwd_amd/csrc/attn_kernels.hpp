@@ -188,7 +188,12 @@ constexpr float kRescaleSlack = 8.0f;
 // KST / VST: depth of the K and V rings (VST <= KST <= VST + 1).  V is read
 // after K within a tile, so with one K stage more than V stages the extra
 // look-ahead costs a K tile of LDS rather than a K and a V tile.
-template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT>
+//
+// KVS (V aliasing K, p.v == p.k): one ring of KST K tiles; the PV product
+// reads V^T from the same LDS tile the QK product read K from, so every key
+// row crosses HBM once (VST must equal KST).
+template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT,
+          bool KVS = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
@@ -204,7 +209,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   // for 16-row waves (a 16-key tile fills half of one; the other half gets P = 0).
   constexpr int NPV = (MT == 32) ? 2 * KBLK : (KBLK + 1) / 2;
   constexpr int TILE_ELEMS = KT * D;
-  constexpr int kPerTile = 2 * Copy::kLoads;       // copies per wave per tile (K and V)
+  constexpr int kPerTile = (KVS ? 1 : 2) * Copy::kLoads;  // copies per wave per tile
+  static_assert(!KVS || KST == VST, "a shared K/V ring has one depth");
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
   static_assert(D % 16 == 0 && D >= 16, "head dim must be a multiple of 16");
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
 
   // V ring first in LDS so that every V transpose read can carry its full LDS
   // offset as an instruction immediate (< 64 KiB); then the K ring.
-  __shared__ __attribute__((aligned(16))) uint16_t vsm[VST][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vsm[KVS ? 1 : VST][KVS ? 8 : TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t ksm[KST][TILE_ELEMS];
 
   const int tid = threadIdx.x;
@@ -278,8 +284,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         kbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
   };
   auto issue_v = [&](int it, int stage, auto j0_c, auto j1_c) {
-    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
-        vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
+    if constexpr (!KVS)
+      Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+          vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
   };
   using All0 = std::integral_constant<int, 0>;
   using AllN = std::integral_constant<int, Copy::kLoads>;
@@ -349,11 +356,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       if constexpr (VROWS == 2) voff[VROWS - 1][db] = 2u * tile_off<D>(row1 + 8, col);
     }
   }
-  const uint32_t v_lds = lds_addr((const FMHA_LDS void*)&vsm[0][0]);
+  const uint32_t v_lds = KVS ? lds_addr((const FMHA_LDS void*)&ksm[0][0])
+                             : lds_addr((const FMHA_LDS void*)&vsm[0][0]);
 
   auto tile = [&](auto u_c, int it) {
     constexpr int U = decltype(u_c)::value;  // it % LCM
-    constexpr int KSG = U % KST, STG = U % VST;
+    constexpr int KSG = U % KST, STG = U % VST;  // (equal with a shared ring)
     const int t0 = kbeg + it * KT;
     // This wave's copies of tile `it` have landed (later tiles may still fly),
     // every wave is past its reads of tile it-1, and then everyone's copies of
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     // ahead of the MFMAs.
     constexpr int NU = NPV * DBLK;
     constexpr int RA = NU < 4 ? NU : 4;
-    constexpr bool kVStageImm = (uint32_t)VST * TILE_ELEMS * 2 <= 65536u;
+    constexpr bool kVStageImm = (uint32_t)VST * TILE_ELEMS * 2 <= 65536u;  // (KVS: VST == KST)
     const uint32_t vst = v_lds + (kVStageImm ? 0u : (uint32_t)STG * TILE_ELEMS * 2);
     u32x4 vfrag[NU];
     auto issue_v = [&](auto u_c) {

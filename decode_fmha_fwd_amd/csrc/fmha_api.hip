@@ -219,9 +219,12 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   const hipStream_t st = (hipStream_t)stream;
   if (!grid_fits(p.n_row_blocks, ns_eff, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
 
+  // V aliasing K (the same buffer): at head dim 512 each key row is then
+  // streamed from HBM once and serves both products
+  const bool kv_shared = (k == v) && D == 512;
   if (ns_eff <= 1) {
     dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
-    return launch_decode(D, c, p, grid, causal != 0, false, st);
+    return launch_decode(D, c, p, grid, causal != 0, false, kv_shared, st);
   }
 
   const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns);
@@ -233,7 +236,7 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + round_up(rows * ns * D * sizeof(float), kAlign));
   dim3 grid((unsigned)p.n_row_blocks * ns_eff * Hkv * B);
-  s = launch_decode(D, c, p, grid, causal != 0, true, st);
+  s = launch_decode(D, c, p, grid, causal != 0, true, kv_shared, st);
   if (s != FMHA_OK) return s;
   return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
                         fp4_scales, fp4_gscale, (long long)rows, ns_eff, st);

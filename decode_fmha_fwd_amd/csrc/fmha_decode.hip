@@ -9,27 +9,30 @@
 namespace fmha {
 namespace {
 
-template <int D, int MT, int NW, int KT, int KS, int VS, bool C, bool S>
+template <int D, int MT, int NW, int KT, int KS, int VS, bool C, bool S, bool KVS>
 fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, S>), grid, dim3(NW * 64), 0, st,
-                     p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, S, KVS>), grid, dim3(NW * 64),
+                     0, st, p);
   return check_launch("attention kernel launch");
 }
 
-template <int D, int MT, int NW, int KT, int KS, int VS>
+template <int D, int MT, int NW, int KT, int KS, int VS, bool KVS = false>
 fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
                            hipStream_t st) {
   if (causal)
-    return split ? launch_attn<D, MT, NW, KT, KS, VS, true, true>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, KS, VS, true, false>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, KS, VS, false, true>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, KS, VS, false, false>(p, grid, st);
+    return split ? launch_attn<D, MT, NW, KT, KS, VS, true, true, KVS>(p, grid, st)
+                 : launch_attn<D, MT, NW, KT, KS, VS, true, false, KVS>(p, grid, st);
+  return split ? launch_attn<D, MT, NW, KT, KS, VS, false, true, KVS>(p, grid, st)
+               : launch_attn<D, MT, NW, KT, KS, VS, false, false, KVS>(p, grid, st);
 }
 
 }  // namespace
 
 fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
-                            bool split, hipStream_t st) {
+                            bool split, bool kv_shared, hipStream_t st) {
+  // V aliasing K at head dim 512: one 5-deep ring of 32-key tiles (160 KB)
+  if (D == 512 && kv_shared)
+    return launch_attn_cs<512, 16, 4, 32, 5, 5, true>(p, grid, causal, split, st);
   if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 32, 3, 3>(p, grid, causal, split, st);
   if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3, 3>(p, grid, causal, split, st);
   if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2, 2>(p, grid, causal, split, st);

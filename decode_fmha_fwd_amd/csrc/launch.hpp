@@ -57,7 +57,7 @@ fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_o
 
 // fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
 fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
-                          bool split, hipStream_t st);
+                          bool split, bool kv_shared, hipStream_t st);
 fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,
                            float* lse, float* o_amax, uint8_t* fp4_codes, uint8_t* fp4_scales,
                            const float* fp4_gscale, long long nrows, int nsplit,

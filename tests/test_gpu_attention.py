@@ -29,7 +29,8 @@ def run_fwd(q, k, v, scale, causal):
 
 def run_decode(q, k, v, scale, causal, num_splits, o_amax=None):
     dev = require_gpu()
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    qd, kd = q.to(dev), k.to(dev)
+    vd = kd if v is k else v.to(dev)  # V aliasing K stays one buffer
     B, Hq, Sq, D = q.shape
     _, Hkv, Sk, _ = k.shape
     o = poison_like(qd)
@@ -157,6 +158,45 @@ def test_decode_workloads_sampled(name):
     o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal, rows=rows)
     assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=name)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+VK_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, num_splits -- V is the same tensor as K
+    (1, 64, 1, 1, 777, 512, False, 4),
+    (1, 64, 1, 1, 300, 512, False, 1),
+    (2, 32, 2, 1, 500, 512, False, 3),
+    (1, 32, 1, 2, 400, 512, True, 2),
+    (2, 8, 2, 1, 300, 64, False, 2),    # other head dims take the two-ring path
+]
+
+
+@pytest.mark.parametrize("case", VK_CASES)
+def test_decode_v_aliasing_k(case):
+    """V passed as the very K buffer (a shared latent): at head dim 512 the
+    kernel streams each key row once and reads V^T from the K tile."""
+    B, Hq, Hkv, Sq, Sk, D, causal, ns = case
+    dev = require_gpu()
+    q, k, _ = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=sum(case) + 1, sigma=0.7)
+    scale = default_scale(D)
+    qd, kd = q.to(dev), k.to(dev)
+    o = poison_like(qd)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    nb = F.fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns)
+    ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=dev)
+    F.fmha_decode_splitkv(qd, kd, kd, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, ns, ws, nb)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_rows(q, k, k, scale, causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=str(case))
+
+
+def test_decode_v_is_k_workload_sampled():
+    w = WORKLOADS["decode_mqa_d512_v_is_k"]
+    q, k, v = make_workload_inputs(w)
+    assert v is k
+    o, lse = run_decode(q, k, v, w.scale, w.causal, w.num_splits)
+    rows = sample_rows(w.B * w.Hq * w.Sq, 64, seed=13)
+    o_ref, lse_ref = oracle_rows(q, k, k, w.scale, w.causal, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=w.name)
 
 
 def test_split_count_does_not_change_the_result():

@@ -33,6 +33,7 @@ class Workload:
     seed: int
     causal: bool
     num_splits: int = 0  # decode only; 0 = the library's heuristic
+    v_is_k: bool = False  # V is the same tensor as K (a shared latent)
     note: str = ""
 
     @property
@@ -58,7 +59,7 @@ class Workload:
         written once; the NVFP4 workload adds the codes, scales and the global
         scale."""
         q = self.B * self.Hq * self.Sq * self.D
-        kv = self.B * self.Hkv * self.Sk * (self.D + self.Dv)
+        kv = self.B * self.Hkv * self.Sk * (self.D if self.v_is_k else self.D + self.Dv)
         o = self.B * self.Hq * self.Sq * self.Dv
         n = 2 * (q + kv + o) + 4 * self.B * self.Hq * self.Sq
         if self.kind == "decode_nvfp4":
@@ -68,7 +69,7 @@ class Workload:
         return n
 
     def kv_bytes(self) -> int:
-        return 2 * self.B * self.Hkv * self.Sk * (self.D + self.Dv)
+        return 2 * self.B * self.Hkv * self.Sk * (self.D if self.v_is_k else self.D + self.Dv)
 
 
 def default_scale(D: int) -> float:
@@ -93,6 +94,10 @@ WORKLOADS = {
                  1.0, 4, False, num_splits=1,
                  note="the same decode with NVFP4 encoded in its epilogue for a global scale "
                       "held from an earlier step; no bf16 O written"),
+        Workload("decode_mqa_d512_v_is_k", "decode", 32, 64, 1, 1, 16384, 512, 512, 0.5, 3, False,
+                 v_is_k=True,
+                 note="the wide-head decode with V the same tensor as K (a shared latent): "
+                      "each key row is streamed once"),
     ]
 }
 
@@ -112,7 +117,8 @@ def make_qkv(B, Hq, Hkv, Sq, Sk, D, Dv=None, *, sigma=1.0, seed=0):
 
 
 def make_workload_inputs(w: Workload):
-    return make_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.Dv, sigma=w.sigma, seed=w.seed)
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.Dv, sigma=w.sigma, seed=w.seed)
+    return (q, k, k) if w.v_is_k else (q, k, v)
 
 
 def sample_rows(total: int, n: int, seed: int = 1234) -> np.ndarray:
