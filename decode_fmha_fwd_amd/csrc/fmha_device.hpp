@@ -144,25 +144,13 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-// LDS transpose read of four bf16 (see the header comment).
-__device__ inline u32x2 lds_read_tr16(const FMHA_LDS void* p) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FMHA_LDS i16x4*)p);
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// The same transpose read issued from inline asm.  The compiler cannot tell
-// which LDS bytes a transpose-read builtin touches, so it would wait for every
-// outstanding global->LDS copy (vmcnt(0)) before each one, serialising the
-// prefetch ring; from asm it inserts nothing, and the caller must wait with
-// lds_wait_tied before using the result.
-__device__ inline u32x2 lds_read_tr16_async(uint32_t lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
-  return r;
-}
-
-// The transpose read with a constant LDS byte offset folded into the
-// instruction (offset < 64 KiB).
+// The LDS transpose read of four bf16 (see the header comment), issued from
+// inline asm: the compiler cannot tell which LDS bytes a transpose-read
+// builtin touches, so it would wait for every outstanding global->LDS copy
+// (vmcnt(0)) before each one, serialising the prefetch ring; from asm it
+// inserts nothing, and the caller must wait (lds_wait_tied) before using the
+// result.  A constant LDS byte offset is folded into the instruction
+// (offset < 64 KiB).
 template <uint32_t OFF>
 __device__ inline u32x2 lds_read_tr16_imm(uint32_t lds_addr) {
   static_assert(OFF < 65536u, "DS offset field is 16 bits");
@@ -214,10 +202,6 @@ __device__ inline u32x4 lds_read_b128(const FMHA_LDS void* p) {
 }
 
 __device__ inline void lds_write_b128(FMHA_LDS void* p, u32x4 v) { *(FMHA_LDS u32x4*)p = v; }
-
-__device__ inline u32x4 global_load_b128(const void* p) {
-  return __builtin_nontemporal_load((const u32x4*)p);
-}
 
 // Asynchronous global -> LDS copy of 16 (or 4) bytes per lane
 // (global_load_lds_dwordx4 / _dword): lane l's bytes land at lds_base +
