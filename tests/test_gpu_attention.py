@@ -86,6 +86,8 @@ FWD_CASES = [
     (1, 2, 2, 190, 300, 128, False),
     (1, 1, 1, 64, 1, 64, False),        # one key
     (3, 3, 1, 45, 45, 128, True),
+    (1, 2, 1, 300, 100, 64, False),     # more queries than keys
+    (2, 6, 3, 129, 129, 32, True),      # odd group size, one row past a 128-row block
 ]
 
 
@@ -136,6 +138,10 @@ DEC_CASES = [
     (1, 2, 1, 1, 40, 64, False, 8),     # more splits than tiles: empty ranges
     (1, 4, 1, 1, 2400, 64, False, 75),  # more than 64 splits: the combine's second pass
     (1, 64, 1, 1, 4200, 512, False, 70),  # 66 effective splits at head dim 512
+    (2, 6, 2, 1, 500, 64, False, 2),    # 3 rows per KV head
+    (1, 128, 1, 1, 300, 64, False, 2),  # 128 rows per KV head: two 64-row workgroups
+    (1, 128, 1, 1, 300, 512, False, 2),  # the same at head dim 512
+    (2, 8, 8, 3, 200, 128, False, 2),   # Sq = 3 without a mask
 ]
 
 
