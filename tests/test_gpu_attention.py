@@ -88,6 +88,12 @@ FWD_CASES = [
     (3, 3, 1, 45, 45, 128, True),
     (1, 2, 1, 300, 100, 64, False),     # more queries than keys
     (2, 6, 3, 129, 129, 32, True),      # odd group size, one row past a 128-row block
+    # head dim 64 (256-row workgroups of two alternating wave groups)
+    (1, 2, 2, 600, 600, 64, True),      # three row blocks, the last ragged
+    (2, 2, 2, 512, 512, 64, True),      # whole row blocks
+    (1, 8, 2, 100, 100, 64, True),      # GQA: one row block spans four heads
+    (1, 1, 1, 64, 1500, 64, False),     # 24 key tiles: the LDS ring wraps several times
+    (1, 2, 1, 70, 1000, 64, True),      # few queries, long causal key range
 ]
 
 
