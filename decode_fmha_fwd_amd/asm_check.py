@@ -11,9 +11,12 @@ path no instruction touches its destination registers before an
 ``s_waitcnt`` that covers it:
 
 * LDS operations complete in issue order, so after ``s_waitcnt lgkmcnt(n)`` a
-  read is complete when at least ``n`` LGKM-counted operations were issued after
-  it on the path (scalar memory loads return out of order, so with one of those
-  issued after the read only ``lgkmcnt(0)`` counts);
+  read is complete when at least ``n`` LDS operations were issued after it on
+  the path: were it still pending, so would be every LDS operation after it,
+  and the counter would exceed ``n``.  Scalar memory loads (and other
+  LGKM-counted operations that return out of order) do not count towards
+  ``n``; while pending they only raise the counter, so they never let such a
+  wait pass early;
 * each function is split into basic blocks at labels and branches, and the
   set of pending reads is propagated along every edge to a fixed point; where
   paths join, a read pending on any incoming path is pending, with the fewest
@@ -48,12 +51,10 @@ def _vregs(text: str) -> set[int]:
 
 
 def _lgkm_op(mnem: str) -> str | None:
-    """'lds' for in-order LGKM operations, 'smem' for out-of-order ones."""
-    if mnem.startswith("ds_") or mnem.startswith("flat_"):
+    """'lds' for LGKM operations that complete in order with the LDS reads
+    (only these count towards a partial wait); None otherwise."""
+    if mnem.startswith("ds_"):
         return "lds"
-    if mnem.startswith(("s_load", "s_buffer_load", "s_scratch_load", "s_memtime",
-                        "s_memrealtime", "s_sendmsg", "s_get_barrier_state")):
-        return "smem"
     return None
 
 
@@ -79,7 +80,7 @@ class Report:
     problems: list[str] = field(default_factory=list)
 
 
-# pending state: read line -> (dest regs, LGKM ops after it, scalar load after it)
+# pending state: read line -> [dest regs, LDS operations issued after it]
 _State = dict
 
 
@@ -154,7 +155,7 @@ def _transfer(block: _Block, state: _State, func: str, name: str, rep: Report | 
             m = _LGKM.search(ins.ops)
             if m:
                 n = int(m.group(1))
-                st = {k: v for k, v in st.items() if not (v[1] >= n and (n == 0 or not v[2]))}
+                st = {k: v for k, v in st.items() if not v[1] >= n}
             continue
         # An LDS read's own destination may overlap a pending LDS read: LDS
         # returns in order, so the later value lands last.  Any other write
@@ -162,18 +163,16 @@ def _transfer(block: _Block, state: _State, func: str, name: str, rep: Report | 
         used = (_vregs(ins.ops.split(",", 1)[1]) if ins.mnem.startswith("ds_read") and "," in ins.ops
                 else _vregs(ins.ops))
         if rep is not None:
-            for line, (regs, _, _) in st.items():
+            for line, (regs, _) in st.items():
                 if regs & used:
                     rep.problems.append(
                         f"{name}:{ins.line}: {func}: '{ins.text}' uses v{sorted(regs)} of the LDS "
                         f"read at line {line} before its wait")
-        kind = _lgkm_op(ins.mnem)
-        if kind:
+        if _lgkm_op(ins.mnem):
             for v in st.values():
                 v[1] += 1
-                v[2] = v[2] or kind == "smem"
         if ins.in_asm and ins.mnem.startswith("ds_read"):
-            st[ins.line] = [_vregs(ins.ops.split(",", 1)[0]), 0, False]
+            st[ins.line] = [_vregs(ins.ops.split(",", 1)[0]), 0]
     return st
 
 
@@ -182,7 +181,6 @@ def _join(a: _State, b: _State) -> _State:
     for k, v in b.items():
         if k in out:
             out[k][1] = min(out[k][1], v[1])
-            out[k][2] = out[k][2] or v[2]
         else:
             out[k] = list(v)
     return out

@@ -47,6 +47,21 @@ def test_write_to_destination_and_scalar_loads():
     smem = check_text(_asm(*READ, "s_load_dword s4, s[0:1], 0x0", "s_waitcnt lgkmcnt(1)",
                            "v_mov_b32_e32 v9, v0", "s_waitcnt lgkmcnt(0)"))
     assert len(smem.problems) == 1
+    # ... nor does a pending scalar load issued before it
+    before = check_text(_asm("s_load_dword s4, s[0:1], 0x0", *READ, "s_waitcnt lgkmcnt(1)",
+                             "v_mov_b32_e32 v9, v0", "s_waitcnt lgkmcnt(0)"))
+    assert len(before.problems) == 1
+
+
+def test_scalar_load_between_reads_does_not_void_a_partial_wait():
+    # READ, scalar load, READ2, lgkmcnt(1): one LDS read follows READ, so READ
+    # is complete (a pending scalar load only raises the counter); READ2 is not
+    ok = check_text(_asm(*READ, "s_load_dword s4, s[0:1], 0x0", *READ2, "s_waitcnt lgkmcnt(1)",
+                         "v_mov_b32_e32 v9, v0", "s_waitcnt lgkmcnt(0)", "v_mov_b32_e32 v9, v2"))
+    assert ok.problems == []
+    bad = check_text(_asm(*READ, "s_load_dword s4, s[0:1], 0x0", *READ2, "s_waitcnt lgkmcnt(1)",
+                          "v_mov_b32_e32 v9, v2", "s_waitcnt lgkmcnt(0)"))
+    assert len(bad.problems) == 1
 
 
 def test_use_on_a_branch_path_before_the_wait_is_flagged():
