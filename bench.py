@@ -25,7 +25,8 @@ import time
 METRIC = "FMHA TFLOP/s (prefill) and KV GB/s (decode) at hd=64/512 on 1 MI355X"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["attn_kernels.hpp", "fmha_device.hpp", "launch.hpp", "fmha_prefill.hip",
-                  "fmha_decode.hip", "nvfp4.hip", "nvfp4_device.hpp", "fmha_api.hip"]
+                  "fmha_decode.hip", "nvfp4.hip", "nvfp4_device.hpp", "fmha_api.hip",
+                  "decode_launch.hpp", "fmha_decode_paged.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_workloads.md")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
@@ -54,12 +55,23 @@ class Runner:
         import torch
 
         import decode_fmha_fwd_amd as F
-        from workloads import make_workload_inputs
+        from workloads import make_workload_inputs, page_pool
 
         self.w, self.F, self.torch = w, F, torch
         q, k, v = make_workload_inputs(w)
-        self.q, self.k = q.to(dev), k.to(dev)
-        self.v = self.k if w.v_is_k else v.to(dev)  # one buffer when V is K
+        self.q = q.to(dev)
+        if w.kind == "decode_paged":
+            # the same K/V as a paged cache in shuffled page order
+            kc, vc, table, self.num_pages = page_pool(k, v, [w.Sk] * w.B, w.page_size,
+                                                      seed=w.seed)
+            self.k, self.v = kc.to(dev), vc.to(dev)
+            del kc, vc
+            self.table = torch.from_numpy(table).to(dev)
+            self.max_pages = table.shape[1]
+            self.seqlens = torch.full((w.B,), w.Sk, dtype=torch.int32, device=dev)
+        else:
+            self.k = k.to(dev)
+            self.v = self.k if w.v_is_k else v.to(dev)  # one buffer when V is K
         del q, k, v
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
@@ -97,6 +109,11 @@ class Runner:
         elif w.kind == "decode":
             F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
                                   w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws, self.ws_bytes)
+        elif w.kind == "decode_paged":
+            F.fmha_decode_paged(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
+                                self.seqlens, self.table, self.max_pages, w.page_size,
+                                self.num_pages, w.D, w.scale, w.causal, w.num_splits, self.ws,
+                                self.ws_bytes)
         elif w.kind == "decode_nvfp4_fused":
             F.fmha_decode_splitkv_nvfp4(self.q, self.k, self.v, None, self.lse, w.B, w.Hq, w.Hkv,
                                         w.Sq, w.Sk, w.D, w.scale, w.causal, w.num_splits,
@@ -111,7 +128,7 @@ class Runner:
                              self.amax, None, 0)
 
     def free(self):
-        for n in ("q", "k", "v", "o", "lse", "ws"):
+        for n in ("q", "k", "v", "o", "lse", "ws", "table", "seqlens"):
             setattr(self, n, None)
 
 

@@ -36,6 +36,8 @@ SIGNATURES = {
                                  _P, _P]),
     "fmha_decode_splitkv_nvfp4": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                        _SZ, _P, _P, _P, _P]),
+    "fmha_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
+                               _I, _I, _P, _SZ, _P]),
     "fmha_decode_default_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "nvfp4_quantize_workspace_size": (_SZ, [_LL, _I]),
     "nvfp4_quantize": (_I, [_P, _LL, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -130,6 +132,19 @@ def fmha_decode_splitkv_nvfp4(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, cau
                                          Hkv, Sq, Sk, D, float(scale), int(causal),
                                          int(num_splits), _ptr(workspace), int(workspace_bytes),
                                          _ptr(global_scale), _ptr(codes), _ptr(scales), st))
+
+
+def fmha_decode_paged(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Sq, seqlens_k, block_table,
+                      max_pages_per_seq, page_size, num_pages, D, scale, causal, num_splits,
+                      workspace, workspace_bytes, stream=None):
+    lib = load_library()
+    st = stream if stream is not None else _stream(q.device)
+    _check("fmha_decode_paged",
+           lib.fmha_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq,
+                                 Hkv, Sq, _ptr(seqlens_k), _ptr(block_table),
+                                 int(max_pages_per_seq), int(page_size), int(num_pages), D,
+                                 float(scale), int(causal), int(num_splits), _ptr(workspace),
+                                 int(workspace_bytes), st))
 
 
 def nvfp4_quantize_workspace_size(rows, cols) -> int:

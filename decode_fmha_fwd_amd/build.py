@@ -44,11 +44,14 @@ PER_FILE = {
     # the decode epilogues can encode NVFP4: the same fp32 semantics as nvfp4.hip
     "fmha_decode.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt",
                         "-fno-gpu-flush-denormals-to-zero"],
+    "fmha_decode_paged.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt",
+                              "-fno-gpu-flush-denormals-to-zero"],
     "nvfp4.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                   "-fno-gpu-flush-denormals-to-zero"],
 }
-SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "nvfp4.hip"]
-ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip"}
+SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip",
+           "nvfp4.hip"]
+ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip"}
 
 
 def hipcc() -> str:

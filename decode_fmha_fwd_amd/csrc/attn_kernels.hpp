@@ -192,8 +192,14 @@ constexpr float kRescaleSlack = 8.0f;
 // KVS (V aliasing K, p.v == p.k): one ring of KST K tiles; the PV product
 // reads V^T from the same LDS tile the QK product read K from, so every key
 // row crosses HBM once (VST must equal KST).
+//
+// PAGED: K and V come from a paged cache ([num_pages][Hkv][page_size][D], a
+// block table per batch, a key count per batch); a key tile never straddles
+// two pages (page_size is a multiple of KT) and a head's rows of a page are
+// contiguous, so each tile is one contiguous read after one table lookup,
+// done a tile ahead of its copies.
 template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT,
-          bool KVS = false>
+          bool KVS = false, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
@@ -211,6 +217,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int TILE_ELEMS = KT * D;
   constexpr int kPerTile = (KVS ? 1 : 2) * Copy::kLoads;  // copies per wave per tile
   static_assert(!KVS || KST == VST, "a shared K/V ring has one depth");
+  static_assert(!(KVS && PAGED), "a paged cache keeps K and V apart");
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
   static_assert(D % 16 == 0 && D >= 16, "head dim must be a multiple of 16");
@@ -245,8 +252,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int b = bk / p.Hkv;
 
   const long long bh_kv = (long long)b * p.Hkv + kvh;
-  const uint16_t* __restrict__ kbase = p.k + bh_kv * p.Sk * D;
-  const uint16_t* __restrict__ vbase = p.v + bh_kv * p.Sk * D;
+  // Keys of this batch: Sk, or its own count in a paged cache (at most Sk,
+  // the table's reach).
+  const int Sk = PAGED ? min(max(p.seqlens[b], 0), p.Sk) : p.Sk;
   const long long row_base = bh_kv * p.rows_per_kv;  // flat (b, h, i) id of row 0
 
   const int r_wg0 = rb * ROWS_WG;
@@ -256,11 +264,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_r = r_wave0 + qcol;
   const bool row_ok = my_r < p.rows_per_kv;
   const int my_rc = row_ok ? my_r : p.rows_per_kv - 1;
-  const int diag = p.Sk - p.Sq;  // causal: key j visible to row i iff j <= i + diag
+  const int diag = Sk - p.Sq;  // causal: key j visible to row i iff j <= i + diag
 
   // Key range of this workgroup.
   const int kbeg = split * p.split_len;
-  int kend = min(p.Sk, kbeg + p.split_len);
+  int kend = min(Sk, kbeg + p.split_len);
   int wave_min_last = INT_MAX;  // smallest last-visible key over the wave's rows
   int wave_max_last = INT_MAX;  // largest
   if (CAUSAL) {
@@ -279,14 +287,41 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
 
-  auto issue_k = [&](int it, int stage, auto j0_c, auto j1_c) {
-    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
-        kbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
+  // Where the rows of key tile `it` of a cache start, the index of its first
+  // key relative to that, and the key count its ragged end is clamped to.
+  struct TileSrc {
+    const uint16_t* base;
+    int t0, lim;
   };
-  auto issue_v = [&](int it, int stage, auto j0_c, auto j1_c) {
+  // Page of key tile `it` in a paged cache (a scalar load of the block table;
+  // tiles past the range still get an in-bounds page: the table slot and the
+  // page id are clamped).
+  auto page_of = [&](int it) {
+    if constexpr (PAGED) {
+      const int slot = min(max(kbeg + it * KT, 0) >> p.page_shift, p.bt_stride - 1);
+      return min(max(p.block_table[(long long)b * p.bt_stride + slot], 0), p.num_pages - 1);
+    } else {
+      return 0;
+    }
+  };
+  auto tile_src = [&](const uint16_t* cache, int it, int page) {
+    const int k0 = kbeg + it * KT;
+    if constexpr (PAGED) {
+      const long long row = (((long long)page * p.Hkv + kvh) << p.page_shift) +
+                            (k0 & ((1 << p.page_shift) - 1));
+      return TileSrc{cache + row * D, 0, Sk - k0};
+    } else {
+      return TileSrc{cache + bh_kv * p.Sk * D, k0, Sk};
+    }
+  };
+  auto issue_k = [&](TileSrc src, int stage, auto j0_c, auto j1_c) {
+    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+        src.base, D, 0, src.t0, src.lim, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
+  };
+  auto issue_v = [&](TileSrc src, int stage, auto j0_c, auto j1_c) {
     if constexpr (!KVS)
       Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
-          vbase, D, 0, kbeg + it * KT, p.Sk, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
+          src.base, D, 0, src.t0, src.lim, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
   };
   using All0 = std::integral_constant<int, 0>;
   using AllN = std::integral_constant<int, Copy::kLoads>;
@@ -312,8 +347,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   // Prologue: the first tiles in flight before Q is even loaded.
 #pragma unroll
   for (int s = 0; s < KST - 1; ++s) {
-    if (s < VST - 1 && s < ntiles) issue_v(s, s, All0{}, AllN{});
-    if (s < ntiles) issue_k(s, s, All0{}, AllN{});
+    if (s < VST - 1 && s < ntiles) issue_v(tile_src(p.v, s, page_of(s)), s, All0{}, AllN{});
+    if (s < ntiles) issue_k(tile_src(p.k, s, page_of(s)), s, All0{}, AllN{});
   }
 
   bf16x8 qf[KSTEPS];
@@ -359,16 +394,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const uint32_t v_lds = KVS ? lds_addr((const FMHA_LDS void*)&ksm[0][0])
                              : lds_addr((const FMHA_LDS void*)&vsm[0][0]);
 
+  // Pages of the tiles the current tile issues copies for (paged cache).
+  int page_v = page_of(VST - 1), page_k = page_of(KST - 1);
+
   auto tile = [&](auto u_c, int it) {
     constexpr int U = decltype(u_c)::value;  // it % LCM
     constexpr int KSG = U % KST, STG = U % VST;  // (equal with a shared ring)
     const int t0 = kbeg + it * KT;
+    // Sources of the tiles this one issues copies for; their pages were looked
+    // up a tile ahead (below), so the scalar loads have landed by now.
+    const TileSrc v_next = tile_src(p.v, it + VST - 1, page_v);
+    const TileSrc k_next = tile_src(p.k, it + KST - 1, page_k);
     // This wave's copies of tile `it` have landed (later tiles may still fly),
     // every wave is past its reads of tile it-1, and then everyone's copies of
     // tile `it` are visible.
     wait_vmcnt_at_most<kMaxPending>(pending_after(it));
     wait_lgkmcnt0();
     lds_barrier();
+    if constexpr (PAGED) {
+      page_v = page_of(it + VST);
+      page_k = page_of(it + KST);
+    }
     // Decode spreads the copies for later tiles through this tile's work,
     // V's over the QK steps and K's over the PV steps (same order and count
     // as issuing them all here), so the memory pipeline is fed while the wave
@@ -378,15 +424,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     const bool more_v = it + VST - 1 < ntiles, more_k = it + KST - 1 < ntiles;
     const int v_stage = (U + VST - 1) % VST, k_stage = (U + KST - 1) % KST;
     if constexpr (!kSpread) {
-      if (more_v) issue_v(it + VST - 1, v_stage, All0{}, AllN{});
-      if (more_k) issue_k(it + KST - 1, k_stage, All0{}, AllN{});
+      if (more_v) issue_v(v_next, v_stage, All0{}, AllN{});
+      if (more_k) issue_k(k_next, k_stage, All0{}, AllN{});
     }
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
     if (CAUSAL && t0 > wave_max_last) {
       if constexpr (kSpread) {
-        if (more_v) issue_v(it + VST - 1, v_stage, All0{}, AllN{});
-        if (more_k) issue_k(it + KST - 1, k_stage, All0{}, AllN{});
+        if (more_v) issue_v(v_next, v_stage, All0{}, AllN{});
+        if (more_k) issue_k(k_next, k_stage, All0{}, AllN{});
       }
       return;
     }
@@ -430,7 +476,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     static_for<0, NQC>([&](auto c_c) {
       constexpr int C = decltype(c_c)::value;
       if (kSpread && more_v)  // V copies [C*L/NQC, (C+1)*L/NQC)
-        issue_v(it + VST - 1, v_stage, std::integral_constant<int, C * Copy::kLoads / NQC>{},
+        issue_v(v_next, v_stage, std::integral_constant<int, C * Copy::kLoads / NQC>{},
                 std::integral_constant<int, (C + 1) * Copy::kLoads / NQC>{});
       if constexpr (C + 1 < NQC) read_k(std::integral_constant<int, C + 1>{});
       // chunk C has landed once at most the next chunk's reads are in flight
@@ -553,7 +599,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     static_for<0, NU>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       if (kSpread && more_k)  // K copies [U*L/NU, (U+1)*L/NU)
-        issue_k(it + KST - 1, k_stage, std::integral_constant<int, U * Copy::kLoads / NU>{},
+        issue_k(k_next, k_stage, std::integral_constant<int, U * Copy::kLoads / NU>{},
                 std::integral_constant<int, (U + 1) * Copy::kLoads / NU>{});
       if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
       constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);

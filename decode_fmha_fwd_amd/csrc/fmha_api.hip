@@ -171,14 +171,24 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
 
 namespace {
 
+// A paged K/V cache: per-batch key counts and a block table (device arrays).
+struct PagedDesc {
+  const int* seqlens;
+  const int* block_table;
+  int bt_stride;
+  int page_shift;
+  int num_pages;
+};
+
 // Split-KV decode; with fp4_codes set, the output epilogue (attention kernel
 // without splits, combine kernel with) also writes the NVFP4 encoding of O
-// for the caller's global scale, and o may be null.
+// for the caller's global scale, and o may be null.  With pg set, K and V are
+// paged caches and Sk is the table's reach.
 fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
                         int num_splits, void* workspace, size_t workspace_bytes, float* o_amax,
                         uint8_t* fp4_codes, uint8_t* fp4_scales, const float* fp4_gscale,
-                        void* stream) {
+                        const PagedDesc* pg, void* stream) {
   // o is optional only for the fused NVFP4 output; q stands in for its checks
   fmha_status s = check_common(q, k, v, (o || !fp4_codes) ? o : q, B, Hq, Hkv, Sq, Sk, scale,
                                causal);
@@ -216,15 +226,26 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   p.nsplit = ns_eff;
   p.split_len = split_len;
   p.scale_log2 = scale * kLog2e;
+  if (pg) {
+    p.seqlens = pg->seqlens;
+    p.block_table = pg->block_table;
+    p.bt_stride = pg->bt_stride;
+    p.page_shift = pg->page_shift;
+    p.num_pages = pg->num_pages;
+  }
   const hipStream_t st = (hipStream_t)stream;
   if (!grid_fits(p.n_row_blocks, ns_eff, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
 
   // V aliasing K (the same buffer): at head dim 512 each key row is then
   // streamed from HBM once and serves both products
-  const bool kv_shared = (k == v) && D == 512;
+  const bool kv_shared = !pg && (k == v) && D == 512;
+  auto attention = [&](dim3 grid, bool split) {
+    return pg ? launch_decode_paged(D, c, p, grid, causal != 0, split, st)
+              : launch_decode(D, c, p, grid, causal != 0, split, kv_shared, st);
+  };
   if (ns_eff <= 1) {
     dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
-    return launch_decode(D, c, p, grid, causal != 0, false, kv_shared, st);
+    return attention(grid, false);
   }
 
   const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns);
@@ -236,7 +257,7 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   p.o_part = (float*)workspace;
   p.lse_part = (float*)((char*)workspace + round_up(rows * ns * D * sizeof(float), kAlign));
   dim3 grid((unsigned)p.n_row_blocks * ns_eff * Hkv * B);
-  s = launch_decode(D, c, p, grid, causal != 0, true, kv_shared, st);
+  s = attention(grid, true);
   if (s != FMHA_OK) return s;
   return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
                         fp4_scales, fp4_gscale, (long long)rows, ns_eff, st);
@@ -252,7 +273,8 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, float* o_amax, void* stream) {
   g_last_error[0] = 0;
   return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
-                     workspace, workspace_bytes, o_amax, nullptr, nullptr, nullptr, stream);
+                     workspace, workspace_bytes, o_amax, nullptr, nullptr, nullptr, nullptr,
+                     stream);
 }
 
 fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* v, void* o,
@@ -266,7 +288,35 @@ fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* 
   if (((uintptr_t)codes & 7u) || ((uintptr_t)global_scale & 3u))
     return fail(FMHA_ERR_ALIGN, "codes must be 8-byte aligned and global_scale 4-byte");
   return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
-                     workspace, workspace_bytes, nullptr, codes, scales, global_scale, stream);
+                     workspace, workspace_bytes, nullptr, codes, scales, global_scale, nullptr,
+                     stream);
+}
+
+fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              float* lse, int B, int Hq, int Hkv, int Sq, const int* seqlens_k,
+                              const int* block_table, int max_pages_per_seq, int page_size,
+                              int num_pages, int D, float scale, int causal, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!seqlens_k || !block_table)
+    return fail(FMHA_ERR_NULL, "seqlens_k and block_table must be non-null");
+  if (((uintptr_t)seqlens_k & 3u) || ((uintptr_t)block_table & 3u))
+    return fail(FMHA_ERR_ALIGN, "seqlens_k and block_table must be 4-byte aligned");
+  if (page_size < 64 || page_size > (1 << 24) || (page_size & (page_size - 1)))
+    return fail(FMHA_ERR_ARG, "page_size must be a power of two in [64, 2^24], got %d",
+                page_size);
+  if (max_pages_per_seq < 1 || (long long)max_pages_per_seq * page_size > (1LL << 30))
+    return fail(FMHA_ERR_ARG, "max_pages_per_seq * page_size must be in [page_size, 2^30]");
+  if (num_pages < 1) return fail(FMHA_ERR_ARG, "num_pages must be >= 1, got %d", num_pages);
+  if (Hkv >= 1 && decode_dim_ok(D) &&
+      (long long)num_pages * page_size * Hkv * D >= (1LL << 61))
+    return fail(FMHA_ERR_SHAPE, "cache too large");
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const PagedDesc pg{seqlens_k, block_table, max_pages_per_seq, shift, num_pages};
+  return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Sq, max_pages_per_seq * page_size,
+                     D, scale, causal, num_splits, workspace, workspace_bytes, nullptr, nullptr,
+                     nullptr, nullptr, &pg, stream);
 }
 
 fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,

@@ -2,31 +2,11 @@
 // attention kernels (16-row waves) and of the log-sum-exp combine kernel.
 #include <hip/hip_runtime.h>
 
-#include "attn_kernels.hpp"
-#include "host_common.hpp"
-#include "launch.hpp"
+#include "decode_launch.hpp"
 
 namespace fmha {
-namespace {
 
-template <int D, int MT, int NW, int KT, int KS, int VS, bool C, bool S, bool KVS>
-fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, S, KVS>), grid, dim3(NW * 64),
-                     0, st, p);
-  return check_launch("attention kernel launch");
-}
-
-template <int D, int MT, int NW, int KT, int KS, int VS, bool KVS = false>
-fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
-                           hipStream_t st) {
-  if (causal)
-    return split ? launch_attn<D, MT, NW, KT, KS, VS, true, true, KVS>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, KS, VS, true, false, KVS>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, KS, VS, false, true, KVS>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, KS, VS, false, false, KVS>(p, grid, st);
-}
-
-}  // namespace
+using decode_detail::launch_attn_cs;
 
 fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                             bool split, bool kv_shared, hipStream_t st) {

@@ -30,6 +30,13 @@ struct AttnParams {
   int nsplit;           // key ranges per (batch, KV head)
   int split_len;        // keys per range, a multiple of KT
   float scale_log2;     // scale * log2(e)
+  // Paged KV cache (decode only).  K and V are [num_pages][Hkv][page_size][D];
+  // key j of batch b sits in page block_table[b * bt_stride + j / page_size].
+  const int* seqlens;      // keys per batch [B] (clamped to [0, Sk], Sk = bt_stride * page_size)
+  const int* block_table;  // page ids [B][bt_stride] (clamped to [0, num_pages))
+  int bt_stride;
+  int page_shift;          // log2(page_size); page_size is a power of two >= 64
+  int num_pages;
 };
 
 // Tile configuration of the decode kernel for a head dim and a row count.
@@ -58,6 +65,9 @@ fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_o
 // fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
 fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                           bool split, bool kv_shared, hipStream_t st);
+// The same decode reading K/V from a paged cache (p.seqlens, p.block_table set).
+fmha_status launch_decode_paged(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
+                                bool split, hipStream_t st);
 fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,
                            float* lse, float* o_amax, uint8_t* fp4_codes, uint8_t* fp4_scales,
                            const float* fp4_gscale, long long nrows, int nsplit,

@@ -160,6 +160,38 @@ fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* 
                                       uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
+ * Split-KV decode over a paged, variable-length KV cache: the arithmetic,
+ * splits and combine of fmha_decode_splitkv, with K and V read through a block
+ * table instead of from one contiguous [B, Hkv, Sk, D] tensor each (the cache
+ * layout of a serving loop; the paging itself is not one of the pages' items).
+ *   k_cache, v_cache: bf16 [num_pages, Hkv, page_size, D] (head-major pages:
+ *     a head's keys of one page are contiguous), 16-byte aligned.
+ *   seqlens_k: device int32 [B], the number of keys of each batch; values are
+ *     clamped to [0, max_pages_per_seq * page_size].  A batch with no keys (or,
+ *     causal, a query row that sees none) gets O = 0 and LSE = -inf.
+ *   block_table: device int32 [B, max_pages_per_seq]; key j of batch b, KV
+ *     head h, is row j % page_size of head h of page block_table[b][j / page_size].  Page ids are
+ *     clamped to [0, num_pages), so a bad entry reads a wrong page, never
+ *     outside the cache; only the first ceil(seqlens_k[b] / page_size)
+ *     entries of a row are read.
+ *   page_size: a power of two, at least 64 (a key tile never straddles pages).
+ *   causal: bottom-right aligned per batch (row i sees keys j <= i + len_b - Sq).
+ *   Sk for the split choice and the workspace is max_pages_per_seq * page_size:
+ *     workspace_bytes >= fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq,
+ *     max_pages_per_seq * page_size, D, num_splits).
+ *   D, num_splits, q, o, lse: as fmha_decode_splitkv (no o_amax).
+ * Errors (nothing launched): FMHA_ERR_NULL for a null pointer, FMHA_ERR_ARG
+ * for a page size, page count or table width out of range, and the checks of
+ * fmha_decode_splitkv.  seqlens_k and block_table stay on the device; their
+ * values are not checked on the host.
+ */
+fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              float* lse, int B, int Hq, int Hkv, int Sq, const int* seqlens_k,
+                              const int* block_table, int max_pages_per_seq, int page_size,
+                              int num_pages, int D, float scale, int causal, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the raw score tile S = scale * Q K^T of the first (batch, head),
  * for Sq, Sk <= 128 and D in {16, 32, 64, 128}, computed by the same device
  * routine the attention kernels use for their QK product; s_out is fp32

@@ -49,7 +49,8 @@ def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, what=""):
             lg = lg[rows]
         # a row that sees no key has lse = -inf on both sides
         same_inf = np.isinf(lg) & np.isinf(lse_ref) & (np.sign(lg) == np.sign(lse_ref))
-        lerr = float(np.where(same_inf, 0.0, np.abs(lg - lse_ref)).max())
+        with np.errstate(invalid="ignore"):
+            lerr = float(np.where(same_inf, 0.0, np.abs(lg - lse_ref)).max())
         assert lerr <= LSE_MAX_ABS, f"{what}: LSE max {lerr:.3e}"
     return mx, mean
 

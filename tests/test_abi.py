@@ -71,6 +71,26 @@ def test_decode_validation(kw, status):
     assert call_dec(**kw) == status
 
 
+def call_paged(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, Hq=4, Hkv=1, Sq=1, sl=FAKE, bt=FAKE,
+               mp=8, ps=64, npages=16, D=64, scale=0.125, causal=0, ns=4, ws=None, wsb=0):
+    return F.load_library().fmha_decode_paged(q, k, v, o, lse, B, Hq, Hkv, Sq, sl, bt, mp, ps,
+                                              npages, D, scale, causal, ns, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sl=None), 1), (dict(bt=None), 1), (dict(k=None), 1), (dict(o=None), 1),
+    (dict(sl=FAKE + 2), 5), (dict(bt=FAKE + 1), 5), (dict(k=FAKE + 8), 5),
+    (dict(ps=32), 8), (dict(ps=96), 8), (dict(ps=1 << 25), 8), (dict(mp=0), 8),
+    (dict(npages=0), 8), (dict(mp=1 << 20, ps=1 << 12), 8),
+    (dict(D=16), 3), (dict(Hq=6, Hkv=4), 4),
+    (dict(Sq=600, causal=1), 2),          # causal needs Sq <= max_pages * page_size (512)
+    (dict(ns=4, ws=None, wsb=0), 6),      # 4 splits of 512 keys need a workspace
+])
+def test_paged_decode_validation(kw, status):
+    assert call_paged(**kw) == status
+    assert F.load_library().fmha_last_error()
+
+
 def test_workspace_formula():
     # rows * splits * (D + 1) floats, each section rounded up to 256 bytes
     rows, ns, D = 64 * 32, 16, 64

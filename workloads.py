@@ -21,7 +21,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4", "decode_nvfp4_fused"
+    kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4",
+                         # "decode_nvfp4_fused", "decode_paged"
     B: int
     Hq: int
     Hkv: int
@@ -34,6 +35,7 @@ class Workload:
     causal: bool
     num_splits: int = 0  # decode only; 0 = the library's heuristic
     v_is_k: bool = False  # V is the same tensor as K (a shared latent)
+    page_size: int = 0    # decode_paged: keys per page of the K/V cache
     note: str = ""
 
     @property
@@ -66,6 +68,8 @@ class Workload:
             n += o // 2 + o // 16 + 4
         elif self.kind == "decode_nvfp4_fused":  # codes and scales instead of O; g read
             n += o // 2 + o // 16 + 4 - 2 * o
+        elif self.kind == "decode_paged":  # the block table and the key counts
+            n += 4 * self.B * (-(-self.Sk // self.page_size) + 1)
         return n
 
     def kv_bytes(self) -> int:
@@ -94,6 +98,10 @@ WORKLOADS = {
                  1.0, 4, False, num_splits=1,
                  note="the same decode with NVFP4 encoded in its epilogue for a global scale "
                       "held from an earlier step; no bf16 O written"),
+        Workload("decode_gqa_d64_paged", "decode_paged", 64, 32, 8, 1, 8192, 64, 64, 1.0, 2,
+                 False, num_splits=16, page_size=64,
+                 note="the GQA decode reading K/V through a block table from a shuffled pool "
+                      "of 64-key pages"),
         Workload("decode_mqa_d512_v_is_k", "decode", 32, 64, 1, 1, 16384, 512, 512, 0.5, 3, False,
                  v_is_k=True,
                  note="the wide-head decode with V the same tensor as K (a shared latent): "
@@ -114,6 +122,39 @@ def make_qkv(B, Hq, Hkv, Sq, Sk, D, Dv=None, *, sigma=1.0, seed=0):
         out.append(t.to(torch.bfloat16).contiguous())
         del t
     return tuple(out)
+
+
+def page_pool(k, v, lens, page_size, *, seed, spare_pages=2):
+    """A paged KV cache holding the first lens[b] keys of batch b of the
+    contiguous K/V [B, Hkv, S, D] (bf16, CPU): pools [num_pages, Hkv,
+    page_size, D] whose pages sit in a seeded random order, the block table
+    [B, max_pages] (int32, unused entries -1) and num_pages.  Slots that hold
+    no key (past a sequence's end, and the spare pages) are NaN, so a read
+    outside a sequence shows in the output."""
+    B, Hkv, S, D = k.shape
+    need = [-(-int(n) // page_size) for n in lens]
+    max_pages = max(max(need), 1)
+    num_pages = sum(need) + spare_pages
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    pools = [torch.empty((num_pages, Hkv, page_size, D), dtype=torch.bfloat16) for _ in range(2)]
+    for pool in pools:
+        pool.view(torch.int16).fill_(0x7FC0)  # bf16 quiet NaN
+    table = np.full((B, max_pages), -1, np.int32)
+    nxt = 0
+    for b in range(B):
+        n = int(lens[b])
+        if need[b] == 0:
+            continue
+        pids = perm[nxt:nxt + need[b]]
+        nxt += need[b]
+        table[b, :need[b]] = pids
+        for src, pool in zip((k, v), pools):
+            rows = torch.empty((Hkv, need[b] * page_size, D), dtype=torch.bfloat16)
+            rows.view(torch.int16).fill_(0x7FC0)
+            rows[:, :n] = src[b, :, :n]
+            pool[torch.from_numpy(pids.astype(np.int64))] = (
+                rows.view(Hkv, need[b], page_size, D).permute(1, 0, 2, 3))
+    return pools[0], pools[1], table, num_pages
 
 
 def make_workload_inputs(w: Workload):
