@@ -5,8 +5,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: for the prefill workload one fmha_fwd call; for the
-decode workloads fmha_decode_splitkv (split kernel + log-sum-exp combine); for
-the NVFP4 workload the decode with the amax folded in plus nvfp4_quantize.
+decode workloads fmha_decode_splitkv (split kernel + log-sum-exp combine), or
+its paged, fused-NVFP4 and Dv != D variants; for the NVFP4 workload the decode
+with the amax folded in plus nvfp4_quantize.
 
 The headline line is the causal prefill (B=4, H=16, S=2048, D=64) in TFLOP/s;
 the line also carries, under "workloads", every named workload (time per step,
@@ -73,13 +74,13 @@ class Runner:
             self.k = k.to(dev)
             self.v = self.k if w.v_is_k else v.to(dev)  # one buffer when V is K
         del q, k, v
-        self.o = torch.empty_like(self.q)
+        self.o = torch.empty((w.B, w.Hq, w.Sq, w.Dv), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
         self.ws = None
         self.ws_bytes = 0
         if w.kind != "fwd":
-            self.ws_bytes = F.fmha_decode_splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D,
-                                                                 w.num_splits)
+            self.ws_bytes = F.fmha_decode_splitkv_dv_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk,
+                                                                    w.D, w.Dv, w.num_splits)
             if self.ws_bytes:
                 self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         if w.kind in ("decode_nvfp4", "decode_nvfp4_fused"):
@@ -109,6 +110,10 @@ class Runner:
         elif w.kind == "decode":
             F.fmha_decode_splitkv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
                                   w.Sk, w.D, w.scale, w.causal, w.num_splits, self.ws, self.ws_bytes)
+        elif w.kind == "decode_dv":
+            F.fmha_decode_splitkv_dv(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv,
+                                     w.Sq, w.Sk, w.D, w.Dv, w.scale, w.causal, w.num_splits,
+                                     self.ws, self.ws_bytes)
         elif w.kind == "decode_paged":
             F.fmha_decode_paged(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq,
                                 self.seqlens, self.table, self.max_pages, w.page_size,
@@ -202,9 +207,10 @@ def cpu_baseline(w, target_s):
     import numpy as np
 
     import oracle
-    from workloads import make_workload_inputs, sample_rows
+    from workloads import make_workload_inputs, sample_rows, v_of
 
     q, k, v = make_workload_inputs(w)
+    v = v_of(v, w.Dv)  # V as its own tensor when it is the first Dv columns of K
     qa = q.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
     ka = k.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
     va = v.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)

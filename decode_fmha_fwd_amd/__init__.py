@@ -39,6 +39,9 @@ SIGNATURES = {
     "fmha_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                _I, _I, _P, _SZ, _P]),
     "fmha_decode_default_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "fmha_decode_splitkv_dv_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "fmha_decode_splitkv_dv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                                    _P, _SZ, _P]),
     "nvfp4_quantize_workspace_size": (_SZ, [_LL, _I]),
     "nvfp4_quantize": (_I, [_P, _LL, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "fmha_debug_qk_scores": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
@@ -120,6 +123,21 @@ def fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, n
            lib.fmha_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq,
                                    Sk, D, float(scale), int(causal), int(num_splits),
                                    _ptr(workspace), int(workspace_bytes), _ptr(o_amax), st))
+
+
+def fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, Dv, num_splits) -> int:
+    return load_library().fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, Dv,
+                                                                num_splits)
+
+
+def fmha_decode_splitkv_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, num_splits,
+                           workspace, workspace_bytes, stream=None):
+    lib = load_library()
+    st = stream if stream is not None else _stream(q.device)
+    _check("fmha_decode_splitkv_dv",
+           lib.fmha_decode_splitkv_dv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                      Sq, Sk, D, Dv, float(scale), int(causal), int(num_splits),
+                                      _ptr(workspace), int(workspace_bytes), st))
 
 
 def fmha_decode_splitkv_nvfp4(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
@@ -210,6 +228,25 @@ def decode(q, k, v, *, num_splits=0, causal=False, scale=None, workspace=None, o
     ws = (workspace or DecodeWorkspace()).get(nbytes, q.device)
     fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits, ws,
                         nbytes, o_amax)
+    return o, lse
+
+
+def decode_dv(q, k, v, dv, *, num_splits=0, causal=False, scale=None, workspace=None,
+              want_lse=True):
+    """Split-KV decode with V/O head dim ``dv`` (Q/K: q.shape[-1]) -> (o [B, Hq, Sq, dv],
+    lse).  ``v`` is a [B, Hkv, Sk, dv] tensor, or ``k`` itself, which makes V the
+    first ``dv`` columns of the K rows."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_bf16(n, t)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    scale = (1.0 / D ** 0.5) if scale is None else scale
+    o = torch.empty((B, Hq, Sq, dv), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if want_lse else None
+    nbytes = fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, dv, num_splits)
+    ws = (workspace or DecodeWorkspace()).get(nbytes, q.device)
+    fmha_decode_splitkv_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, dv, scale, causal, num_splits,
+                           ws, nbytes)
     return o, lse
 
 

@@ -47,10 +47,16 @@
 namespace fmha {
 
 
-// log2(min(CPR, 16)): chunk-index bits the swizzle permutes.
+// Chunk-index bits the swizzle permutes for rows of CPR 16-byte chunks: 4 when
+// a row is a whole number of 256-byte bank windows, else the bits of the
+// row's offset within a window that the row index does not already vary (a
+// 576-wide row, 72 chunks, starts each odd row half a window further on, so
+// three bits are left).  CPR is a multiple of 2^bits, so an XORed chunk stays
+// inside its row.
 template <int CPR>
 struct CPR_LOG2 {
-  static constexpr int value = CPR >= 16 ? 4 : (CPR == 8 ? 3 : (CPR == 4 ? 2 : 1));
+  static constexpr int value =
+      (CPR % 16 == 0) ? 4 : (CPR % 8 == 0 ? 3 : (CPR % 4 == 0 ? 2 : 1));
 };
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
@@ -198,25 +204,34 @@ constexpr float kRescaleSlack = 8.0f;
 // two pages (page_size is a multiple of KT) and a head's rows of a page are
 // contiguous, so each tile is one contiguous read after one table lookup,
 // done a tile ahead of its copies.
+//
+// DV: head dim of V and O (D: of Q and K).  With a shared ring (KVS) V is the
+// first DV columns of each K row.
 template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT,
-          bool KVS = false, bool PAGED = false>
+          bool KVS = false, bool PAGED = false, int DV = D>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
   // Decode reads every K/V byte once: stream it non-temporally.  Prefill
   // re-reads K/V from L2 for every row block of a head: keep it cached.
   constexpr bool kStream = (MT == 16);
-  using Copy = TileCopy<D, NW, KT, kStream>;
+  using CopyK = TileCopy<D, NW, KT, kStream>;
+  using CopyV = TileCopy<DV, NW, KT, kStream>;
+  constexpr int VW = KVS ? D : DV;                 // row width of the LDS tile V^T is read from
   constexpr int KSTEPS = (D + M::kK - 1) / M::kK;  // QK contraction steps
   constexpr int KBLK = KT / MT;                    // MT-key blocks per tile
-  constexpr int DBLK = (D + MT - 1) / MT;          // MT-wide head-dim blocks of O^T
+  constexpr int DBLK = (DV + MT - 1) / MT;         // MT-wide head-dim blocks of O^T
   constexpr int ROWS_WG = NW * MT;
   // PV instructions per d-block: 16 keys each for 32-row waves, 32 keys each
   // for 16-row waves (a 16-key tile fills half of one; the other half gets P = 0).
   constexpr int NPV = (MT == 32) ? 2 * KBLK : (KBLK + 1) / 2;
-  constexpr int TILE_ELEMS = KT * D;
-  constexpr int kPerTile = (KVS ? 1 : 2) * Copy::kLoads;  // copies per wave per tile
+  constexpr int KTILE = KT * D;   // elements of a K tile
+  constexpr int VTILE = KT * VW;  // elements of the tile V^T is read from
+  constexpr int nK = CopyK::kLoads, nV = KVS ? 0 : CopyV::kLoads;  // copies per wave per tile
+  constexpr int kPerTile = nK + nV;
   static_assert(!KVS || KST == VST, "a shared K/V ring has one depth");
+  static_assert(DV <= D || !KVS, "V inside the K rows needs DV <= D");
+  static_assert(DV == D || MT == 16, "separate V width: 16-row (decode) waves");
   static_assert(!(KVS && PAGED), "a paged cache keeps K and V apart");
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
@@ -224,14 +239,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   static_assert(VST >= 2 && KST <= 6 && (KST == VST || KST == VST + 1), "ring depths");
   // copies of this wave that may still be in flight when a tile is needed
   constexpr int kMaxPending = (KST == VST) ? (KST - 2) * kPerTile
-                                           : Copy::kLoads + (VST - 2) * kPerTile;
+                                           : nK + (VST - 2) * kPerTile;
   static_assert(kMaxPending < 64, "vmcnt range");
   constexpr int LCM = (KST == VST) ? KST : KST * VST;  // loop unroll: both stages constant
 
   // V ring first in LDS so that every V transpose read can carry its full LDS
   // offset as an instruction immediate (< 64 KiB); then the K ring.
-  __shared__ __attribute__((aligned(16))) uint16_t vsm[KVS ? 1 : VST][KVS ? 8 : TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t ksm[KST][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vsm[KVS ? 1 : VST][KVS ? 8 : VTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ksm[KST][KTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -304,27 +319,29 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       return 0;
     }
   };
-  auto tile_src = [&](const uint16_t* cache, int it, int page) {
+  // (w: row width of the cache, D for K and DV for V)
+  auto tile_src = [&](const uint16_t* cache, int w, int it, int page) {
     const int k0 = kbeg + it * KT;
     if constexpr (PAGED) {
       const long long row = (((long long)page * p.Hkv + kvh) << p.page_shift) +
                             (k0 & ((1 << p.page_shift) - 1));
-      return TileSrc{cache + row * D, 0, Sk - k0};
+      return TileSrc{cache + row * w, 0, Sk - k0};
     } else {
-      return TileSrc{cache + bh_kv * p.Sk * D, k0, Sk};
+      return TileSrc{cache + bh_kv * p.Sk * w, k0, Sk};
     }
   };
   auto issue_k = [&](TileSrc src, int stage, auto j0_c, auto j1_c) {
-    Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+    CopyK::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
         src.base, D, 0, src.t0, src.lim, (FMHA_LDS char*)&ksm[stage][0], wave, lane);
   };
   auto issue_v = [&](TileSrc src, int stage, auto j0_c, auto j1_c) {
     if constexpr (!KVS)
-      Copy::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
-          src.base, D, 0, src.t0, src.lim, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
+      CopyV::template issue<decltype(j0_c)::value, decltype(j1_c)::value>(
+          src.base, DV, 0, src.t0, src.lim, (FMHA_LDS char*)&vsm[stage][0], wave, lane);
   };
   using All0 = std::integral_constant<int, 0>;
-  using AllN = std::integral_constant<int, Copy::kLoads>;
+  using AllK = std::integral_constant<int, nK>;
+  using AllV = std::integral_constant<int, CopyV::kLoads>;
   // Copies of this wave issued after both K(it) and V(it) (see the issue
   // order: prologue V0 K0 V1 K1 ..., then per tile V(it+VST-1), K(it+KST-1)).
   auto pending_after = [&](int it) {
@@ -334,11 +351,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       for (int j = 1; j <= KST - 2; ++j)
         if (it + j < ntiles) n += kPerTile;
     } else {
-      if (it + 1 < ntiles) n += Copy::kLoads;
+      if (it + 1 < ntiles) n += nK;
 #pragma unroll
       for (int j = 1; j <= VST - 2; ++j) {
-        if (it + j < ntiles) n += Copy::kLoads;
-        if (it + j + 1 < ntiles) n += Copy::kLoads;
+        if (it + j < ntiles) n += nV;
+        if (it + j + 1 < ntiles) n += nK;
       }
     }
     return n;
@@ -347,8 +364,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   // Prologue: the first tiles in flight before Q is even loaded.
 #pragma unroll
   for (int s = 0; s < KST - 1; ++s) {
-    if (s < VST - 1 && s < ntiles) issue_v(tile_src(p.v, s, page_of(s)), s, All0{}, AllN{});
-    if (s < ntiles) issue_k(tile_src(p.k, s, page_of(s)), s, All0{}, AllN{});
+    if (s < VST - 1 && s < ntiles) issue_v(tile_src(p.v, DV, s, page_of(s)), s, All0{}, AllV{});
+    if (s < ntiles) issue_k(tile_src(p.k, D, s, page_of(s)), s, All0{}, AllK{});
   }
 
   bf16x8 qf[KSTEPS];
@@ -367,7 +384,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int KSW = CPR_LOG2<D / 8>::value;          // swizzled chunk-index bits
   constexpr int KPER_RAW = (1 << KSW) / (M::kK / 8);   // K-read column period in k-steps
   constexpr int KPER = KPER_RAW < 1 ? 1 : (KPER_RAW > KSTEPS ? KSTEPS : KPER_RAW);
-  constexpr int VPER_RAW = (1 << KSW) / (MT / 8);      // V-read column period in d-blocks
+  constexpr int VSW = CPR_LOG2<VW / 8>::value;          // the same for the V^T tile
+  constexpr int VPER_RAW = (1 << VSW) / (MT / 8);      // V-read column period in d-blocks
   constexpr int VPER = VPER_RAW < 1 ? 1 : (VPER_RAW > DBLK ? DBLK : VPER_RAW);
   constexpr int VROWS = (MT == 32) ? 2 : 1;            // distinct row phases of a V read pair
   uint32_t koff[KPER];  // bytes
@@ -383,12 +401,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < VPER; ++db) {
       int col = (MT == 32) ? db * 32 + 16 * (grp & 1) + 4 * ta : db * 16 + 4 * ta;
-      if (col >= D) col -= D;  // head dims past D (D = 16 with 32-wide blocks): discarded
+      if (col >= DV) col -= DV;  // head dims past DV (16 with 32-wide blocks): discarded
       // MT = 32: k-slots 0..3 <-> keys 16*step + 4h + 0..3, 4..7 <-> 16*step + 8 + 4h + 0..3
       // MT = 16: k-slots 0..3 <-> keys 32*step + 4g + 0..3, 4..7 <-> 32*step + 16 + 4g + 0..3
       const int row1 = (MT == 32) ? 4 * (grp >> 1) + tj : 4 * grp + tj;
-      voff[0][db] = 2u * tile_off<D>(row1, col);
-      if constexpr (VROWS == 2) voff[VROWS - 1][db] = 2u * tile_off<D>(row1 + 8, col);
+      voff[0][db] = 2u * tile_off<VW>(row1, col);
+      if constexpr (VROWS == 2) voff[VROWS - 1][db] = 2u * tile_off<VW>(row1 + 8, col);
     }
   }
   const uint32_t v_lds = KVS ? lds_addr((const FMHA_LDS void*)&ksm[0][0])
@@ -403,8 +421,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     const int t0 = kbeg + it * KT;
     // Sources of the tiles this one issues copies for; their pages were looked
     // up a tile ahead (below), so the scalar loads have landed by now.
-    const TileSrc v_next = tile_src(p.v, it + VST - 1, page_v);
-    const TileSrc k_next = tile_src(p.k, it + KST - 1, page_k);
+    const TileSrc v_next = tile_src(p.v, DV, it + VST - 1, page_v);
+    const TileSrc k_next = tile_src(p.k, D, it + KST - 1, page_k);
     // This wave's copies of tile `it` have landed (later tiles may still fly),
     // every wave is past its reads of tile it-1, and then everyone's copies of
     // tile `it` are visible.
@@ -424,15 +442,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     const bool more_v = it + VST - 1 < ntiles, more_k = it + KST - 1 < ntiles;
     const int v_stage = (U + VST - 1) % VST, k_stage = (U + KST - 1) % KST;
     if constexpr (!kSpread) {
-      if (more_v) issue_v(v_next, v_stage, All0{}, AllN{});
-      if (more_k) issue_k(k_next, k_stage, All0{}, AllN{});
+      if (more_v) issue_v(v_next, v_stage, All0{}, AllV{});
+      if (more_k) issue_k(k_next, k_stage, All0{}, AllK{});
     }
 
     // Causal: a tile entirely past this wave's last visible key adds nothing.
     if (CAUSAL && t0 > wave_max_last) {
       if constexpr (kSpread) {
-        if (more_v) issue_v(v_next, v_stage, All0{}, AllN{});
-        if (more_k) issue_k(k_next, k_stage, All0{}, AllN{});
+        if (more_v) issue_v(v_next, v_stage, All0{}, AllV{});
+        if (more_k) issue_k(k_next, k_stage, All0{}, AllK{});
       }
       return;
     }
@@ -447,8 +465,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     constexpr int NQC = (KSTEPS + QCH - 1) / QCH;
     // Byte offset of this tile's K stage: an instruction immediate when the
     // whole ring fits the 16-bit DS offset, else added once per tile.
-    constexpr uint32_t kStageBytes = (uint32_t)KSG * TILE_ELEMS * 2;
-    constexpr bool kStageImm = (uint32_t)KST * TILE_ELEMS * 2 <= 65536u;
+    constexpr uint32_t kStageBytes = (uint32_t)KSG * KTILE * 2;
+    constexpr bool kStageImm = (uint32_t)KST * KTILE * 2 <= 65536u;
     const uint32_t kst = k_lds + (kStageImm ? 0u : kStageBytes);
     u32x4 kf[NQC][KBLK][QCH];
     auto read_k = [&](auto c_c) {
@@ -476,8 +494,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     static_for<0, NQC>([&](auto c_c) {
       constexpr int C = decltype(c_c)::value;
       if (kSpread && more_v)  // V copies [C*L/NQC, (C+1)*L/NQC)
-        issue_v(v_next, v_stage, std::integral_constant<int, C * Copy::kLoads / NQC>{},
-                std::integral_constant<int, (C + 1) * Copy::kLoads / NQC>{});
+        issue_v(v_next, v_stage, std::integral_constant<int, C * CopyV::kLoads / NQC>{},
+                std::integral_constant<int, (C + 1) * CopyV::kLoads / NQC>{});
       if constexpr (C + 1 < NQC) read_k(std::integral_constant<int, C + 1>{});
       // chunk C has landed once at most the next chunk's reads are in flight
       constexpr int kNext = (C + 1 < NQC) ? KBLK * ((KSTEPS - (C + 1) * QCH) < QCH
@@ -575,20 +593,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     // ahead of the MFMAs.
     constexpr int NU = NPV * DBLK;
     constexpr int RA = NU < 4 ? NU : 4;
-    constexpr bool kVStageImm = (uint32_t)VST * TILE_ELEMS * 2 <= 65536u;  // (KVS: VST == KST)
-    const uint32_t vst = v_lds + (kVStageImm ? 0u : (uint32_t)STG * TILE_ELEMS * 2);
+    constexpr bool kVStageImm = (uint32_t)VST * VTILE * 2 <= 65536u;  // (KVS: VST == KST)
+    const uint32_t vst = v_lds + (kVStageImm ? 0u : (uint32_t)STG * VTILE * 2);
     u32x4 vfrag[NU];
     auto issue_v = [&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       constexpr int step = U / DBLK, db = U % DBLK;
       // stage offset: an instruction immediate when the V ring fits the 16-bit
       // DS offset, else folded into the per-tile base vst
-      constexpr uint32_t stage_bytes = kVStageImm ? (uint32_t)STG * TILE_ELEMS * 2 : 0u;
-      constexpr uint32_t row_step = (MT == 32) ? 16u * D * 2 : 32u * D * 2;
+      constexpr uint32_t stage_bytes = kVStageImm ? (uint32_t)STG * VTILE * 2 : 0u;
+      constexpr uint32_t row_step = (MT == 32) ? 16u * VW * 2 : 32u * VW * 2;
       constexpr uint32_t col_step = (uint32_t)(db / VPER) * VPER * MT * 2;
       constexpr uint32_t imm1 = stage_bytes + step * row_step + col_step;
       // (a half-filled 32-deep step re-reads its own rows for the zero-P half)
-      constexpr uint32_t imm2 = imm1 + ((MT == 32 || KT == 16) ? 0u : 16u * D * 2);
+      constexpr uint32_t imm2 = imm1 + ((MT == 32 || KT == 16) ? 0u : 16u * VW * 2);
       const uint32_t a1 = vst + voff[0][db % VPER];
       const u32x2 lo = lds_read_tr16_imm<imm1>(a1);
       const uint32_t a2 = vst + voff[VROWS - 1][db % VPER];
@@ -599,8 +617,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     static_for<0, NU>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       if (kSpread && more_k)  // K copies [U*L/NU, (U+1)*L/NU)
-        issue_k(k_next, k_stage, std::integral_constant<int, U * Copy::kLoads / NU>{},
-                std::integral_constant<int, (U + 1) * Copy::kLoads / NU>{});
+        issue_k(k_next, k_stage, std::integral_constant<int, U * nK / NU>{},
+                std::integral_constant<int, (U + 1) * nK / NU>{});
       if constexpr (U + RA < NU) issue_v(std::integral_constant<int, U + RA>{});
       constexpr int pending = 2 * ((NU - 1 - U) < RA ? (NU - 1 - U) : RA);
       lds_wait_tied<pending>(vfrag[U]);
@@ -629,15 +647,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int qd = 0; qd < M::kRegs / 4; ++qd) {
         const int d0 = (MT == 32) ? db * 32 + 8 * qd + 4 * kg : db * 16 + 4 * kg;
-        if (d0 >= D) continue;
+        if (d0 >= DV) continue;
         const float o0 = oacc[db][4 * qd + 0] * inv, o1 = oacc[db][4 * qd + 1] * inv;
         const float o2 = oacc[db][4 * qd + 2] * inv, o3 = oacc[db][4 * qd + 3] * inv;
         if constexpr (SPLIT) {
-          float* dst = p.o_part + ((row_base + my_r) * p.nsplit + split) * D + d0;
+          float* dst = p.o_part + ((row_base + my_r) * p.nsplit + split) * DV + d0;
           *(f32x4*)dst = f32x4{o0, o1, o2, o3};
         } else {
           const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
-          if (p.o) *(u32x2*)(p.o + (row_base + my_r) * D + d0) = u32x2{w0, w1};
+          if (p.o) *(u32x2*)(p.o + (row_base + my_r) * DV + d0) = u32x2{w0, w1};
           if (p.o_amax) {
             amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
             amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
@@ -684,8 +702,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
                            (nvfp4_code(x2, sc, t) << 8) | (nvfp4_code(x3, sc, t) << 12);
         if (row_ok) {
           const long long r = row_base + my_r;
-          *(uint16_t*)(p.fp4_codes + r * (D / 2) + db * 8 + 2 * kg) = (uint16_t)c;
-          if (kg == 0) p.fp4_scales[r * (D / 16) + db] = (uint8_t)sc;
+          *(uint16_t*)(p.fp4_codes + r * (DV / 2) + db * 8 + 2 * kg) = (uint16_t)c;
+          if (kg == 0) p.fp4_scales[r * (DV / 16) + db] = (uint8_t)sc;
         }
       }
     }

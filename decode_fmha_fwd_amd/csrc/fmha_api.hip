@@ -38,6 +38,8 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool decode_dim_ok(int D) { return D == 64 || D == 128 || D == 512; }
+// (Q/K head dim, V/O head dim) pairs the decode kernels are built for.
+bool decode_dims_ok(int D, int Dv) { return (Dv == D && decode_dim_ok(D)) || (D == 576 && Dv == 512); }
 bool fwd_dim_ok(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
 fmha_status check_common(const void* q, const void* k, const void* v, const void* o, int B,
@@ -155,16 +157,22 @@ int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   return default_splits(B, Hq, Hkv, Sq, Sk, D);
 }
 
-size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
-                                          int num_splits) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv || !decode_dim_ok(D) ||
+size_t fmha_decode_splitkv_dv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                             int Dv, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || Hq % Hkv || !decode_dims_ok(D, Dv) ||
       num_splits < 0 || num_splits > 1024)
     return 0;
   int ns = num_splits ? num_splits : default_splits(B, Hq, Hkv, Sq, Sk, D);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * Hq * Sq;
-  return round_up(rows * ns * D * sizeof(float), kAlign) +
+  return round_up(rows * ns * Dv * sizeof(float), kAlign) +
          round_up(rows * ns * sizeof(float), kAlign);
+}
+
+size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                          int num_splits) {
+  if (!decode_dim_ok(D)) return 0;
+  return fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, D, num_splits);
 }
 
 }  // extern "C"
@@ -185,7 +193,7 @@ struct PagedDesc {
 // for the caller's global scale, and o may be null.  With pg set, K and V are
 // paged caches and Sk is the table's reach.
 fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                        int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale, int causal,
                         int num_splits, void* workspace, size_t workspace_bytes, float* o_amax,
                         uint8_t* fp4_codes, uint8_t* fp4_scales, const float* fp4_gscale,
                         const PagedDesc* pg, void* stream) {
@@ -195,11 +203,16 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   if (s != FMHA_OK) return s;
   if (lse && !aligned16(lse)) return fail(FMHA_ERR_ALIGN, "lse must be 16-byte aligned");
   if (o_amax && ((uintptr_t)o_amax & 3)) return fail(FMHA_ERR_ALIGN, "o_amax must be 4-byte aligned");
-  if (!decode_dim_ok(D))
-    return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv supports D in {64,128,512}, got %d", D);
+  if (!decode_dims_ok(D, Dv))
+    return fail(FMHA_ERR_HEAD_DIM,
+                "decode supports D = Dv in {64,128,512} and (D, Dv) = (576, 512), got (%d, %d)",
+                D, Dv);
+  if (Dv != D && (pg || fp4_codes || o_amax))
+    return fail(FMHA_ERR_HEAD_DIM, "Dv != D is built for the plain split-KV decode only");
   if (num_splits < 0 || num_splits > 1024)
     return fail(FMHA_ERR_ARG, "num_splits must be in 0..1024, got %d", num_splits);
-  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D)) return fail(FMHA_ERR_SHAPE, "tensor too large");
+  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D > Dv ? D : Dv))
+    return fail(FMHA_ERR_SHAPE, "tensor too large");
 
   const int rows_per_kv = (Hq / Hkv) * Sq;
   const DecodeCfg c = decode_cfg(D, rows_per_kv);
@@ -236,30 +249,31 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   const hipStream_t st = (hipStream_t)stream;
   if (!grid_fits(p.n_row_blocks, ns_eff, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
 
-  // V aliasing K (the same buffer): at head dim 512 each key row is then
-  // streamed from HBM once and serves both products
-  const bool kv_shared = !pg && (k == v) && D == 512;
+  // V aliasing K (the same buffer): at head dim 512, or with V the first Dv
+  // columns of the K rows, each key row is then streamed from HBM once and
+  // serves both products
+  const bool kv_shared = !pg && (k == v) && (D == 512 || Dv < D);
   auto attention = [&](dim3 grid, bool split) {
     return pg ? launch_decode_paged(D, c, p, grid, causal != 0, split, st)
-              : launch_decode(D, c, p, grid, causal != 0, split, kv_shared, st);
+              : launch_decode(D, Dv, c, p, grid, causal != 0, split, kv_shared, st);
   };
   if (ns_eff <= 1) {
     dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
     return attention(grid, false);
   }
 
-  const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, ns);
+  const size_t need = fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, Dv, ns);
   if (!workspace || workspace_bytes < need)
     return fail(FMHA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(FMHA_ERR_ALIGN, "workspace must be 16-byte aligned");
   const size_t rows = (size_t)B * Hq * Sq;
   p.o_part = (float*)workspace;
-  p.lse_part = (float*)((char*)workspace + round_up(rows * ns * D * sizeof(float), kAlign));
+  p.lse_part = (float*)((char*)workspace + round_up(rows * ns * Dv * sizeof(float), kAlign));
   dim3 grid((unsigned)p.n_row_blocks * ns_eff * Hkv * B);
   s = attention(grid, true);
   if (s != FMHA_OK) return s;
-  return launch_combine(D, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
+  return launch_combine(Dv, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
                         fp4_scales, fp4_gscale, (long long)rows, ns_eff, st);
 }
 
@@ -272,8 +286,19 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 int causal, int num_splits, void* workspace,
                                 size_t workspace_bytes, float* o_amax, void* stream) {
   g_last_error[0] = 0;
-  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+  if (D == 576) return fail(FMHA_ERR_HEAD_DIM, "D = 576 needs Dv: use fmha_decode_splitkv_dv");
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, D, scale, causal, num_splits,
                      workspace, workspace_bytes, o_amax, nullptr, nullptr, nullptr, nullptr,
+                     stream);
+}
+
+fmha_status fmha_decode_splitkv_dv(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                   int Dv, float scale, int causal, int num_splits,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, num_splits,
+                     workspace, workspace_bytes, nullptr, nullptr, nullptr, nullptr, nullptr,
                      stream);
 }
 
@@ -287,7 +312,8 @@ fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* 
     return fail(FMHA_ERR_NULL, "global_scale, codes and scales must be non-null");
   if (((uintptr_t)codes & 7u) || ((uintptr_t)global_scale & 3u))
     return fail(FMHA_ERR_ALIGN, "codes must be 8-byte aligned and global_scale 4-byte");
-  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, num_splits,
+  if (D == 576) return fail(FMHA_ERR_HEAD_DIM, "the fused NVFP4 decode is built for D = Dv");
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, D, scale, causal, num_splits,
                      workspace, workspace_bytes, nullptr, codes, scales, global_scale, nullptr,
                      stream);
 }
@@ -314,8 +340,9 @@ fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   const PagedDesc pg{seqlens_k, block_table, max_pages_per_seq, shift, num_pages};
+  if (D == 576) return fail(FMHA_ERR_HEAD_DIM, "the paged decode is built for D = Dv");
   return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Sq, max_pages_per_seq * page_size,
-                     D, scale, causal, num_splits, workspace, workspace_bytes, nullptr, nullptr,
+                     D, D, scale, causal, num_splits, workspace, workspace_bytes, nullptr, nullptr,
                      nullptr, nullptr, &pg, stream);
 }
 

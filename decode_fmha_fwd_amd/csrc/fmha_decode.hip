@@ -8,8 +8,18 @@ namespace fmha {
 
 using decode_detail::launch_attn_cs;
 
-fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
-                            bool split, bool kv_shared, hipStream_t st) {
+fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 grid,
+                          bool causal, bool split, bool kv_shared, hipStream_t st) {
+  // Q/K head dim 576, V/O head dim 512: a latent of 512 plus 64 more key
+  // dims.  V inside the K rows: one 4-deep ring of 32-key K tiles (144 KB);
+  // separate V: 2-deep K and V rings (136 KB).
+  if (D == 576 && Dv == 512) {
+    if (kv_shared)
+      return launch_attn_cs<576, 16, 4, 32, 4, 4, true, false, 512>(p, grid, causal, split, st);
+    return launch_attn_cs<576, 16, 4, 32, 2, 2, false, false, 512>(p, grid, causal, split, st);
+  }
+  if (Dv != D)
+    return fail(FMHA_ERR_HEAD_DIM, "decode: head dims D=%d, Dv=%d not built", D, Dv);
   // V aliasing K at head dim 512: one 5-deep ring of 32-key tiles (160 KB)
   if (D == 512 && kv_shared)
     return launch_attn_cs<512, 16, 4, 32, 5, 5, true>(p, grid, causal, split, st);

@@ -15,11 +15,11 @@ struct AttnParams {
   const uint16_t* v;
   uint16_t* o;          // bf16 output (no split)
   float* lse;           // fp32 [rows] or null (no split)
-  float* o_part;        // fp32 [rows][nsplit][D] (split)
+  float* o_part;        // fp32 [rows][nsplit][Dv] (split)
   float* lse_part;      // fp32 [rows][nsplit]   (split)
   float* o_amax;        // optional running max |O| (no split)
-  uint8_t* fp4_codes;   // optional fused NVFP4 output: codes [rows][D/2] (no split)
-  uint8_t* fp4_scales;  //   E4M3 block scales [rows][D/16]
+  uint8_t* fp4_codes;   // optional fused NVFP4 output: codes [rows][Dv/2] (no split)
+  uint8_t* fp4_scales;  //   E4M3 block scales [rows][Dv/16]
   const float* fp4_gscale;  //   the caller's global scale (1 float, device)
   int B;
   int Hkv;
@@ -48,11 +48,11 @@ struct DecodeCfg {
 
 // One-wave workgroups when the rows of a KV head fit in one 16-row wave (many
 // small workgroups keep enough loads in flight per CU); four waves otherwise.
-// Head dim 512: four waves sharing 32-key tiles in a 3-deep K ring and a
-// 2-deep V ring (160 KB of LDS, the whole CU).
+// Head dim 512 (and 576 with V/O at 512): four waves sharing 32-key tiles in
+// rings that take most of the CU's 160 KB of LDS.
 // Must match the instantiations in fmha_decode.hip.
 inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
-  if (D == 512) return {4, 32, 1};
+  if (D >= 512) return {4, 32, 1};
   if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 5};
   return {4, 64, D == 64 ? 3 : 2};
 }
@@ -63,8 +63,10 @@ fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_o
                                 int Sk, int D, float scale, hipStream_t st);
 
 // fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
-fmha_status launch_decode(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
-                          bool split, bool kv_shared, hipStream_t st);
+// D: head dim of Q/K, Dv: of V/O; kv_shared: V is the first Dv columns of the
+// K rows (p.v == p.k).
+fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 grid,
+                          bool causal, bool split, bool kv_shared, hipStream_t st);
 // The same decode reading K/V from a paged cache (p.seqlens, p.block_table set).
 fmha_status launch_decode_paged(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                                 bool split, hipStream_t st);

@@ -110,6 +110,31 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
 int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 
 /*
+ * Split-KV decode with a V/O head dimension Dv different from the Q/K head
+ * dimension D.  The page "NVFP4-1.1_RAW_CUDA_CPP_APPROACH.md" singles out head
+ * dimension 512 among its goals, and the workload list names the V head
+ * dimension apart from the Q/K one; the built pair is the shared-latent shape
+ * D = 576, Dv = 512 (a 512-wide latent that serves as V plus 64 more key
+ * dimensions).  The arithmetic is that of fmha_decode_splitkv:
+ *     S[i, j] = scale * sum_{d < D} Q[i, d] * K[j, d],   O[i, :] = sum_j P[i, j] * V[j, :Dv]
+ *   q [B, Hq, Sq, D], k [B, Hkv, Sk, D], o [B, Hq, Sq, Dv], lse [B, Hq, Sq].
+ *   v: either a separate bf16 [B, Hkv, Sk, Dv] tensor, or the very pointer
+ *     passed as k, which makes V the first Dv columns of each K row (row
+ *     stride D): each key row then crosses HBM once and serves both products.
+ *   (D, Dv): (576, 512), or D == Dv in {64, 128, 512} (then exactly
+ *     fmha_decode_splitkv).  Anything else: FMHA_ERR_HEAD_DIM.
+ *   workspace_bytes >= fmha_decode_splitkv_dv_workspace_size(...) (fp32
+ *     partials of width Dv).  num_splits, causal, scale, errors and the
+ *     execution model: as fmha_decode_splitkv.
+ */
+size_t fmha_decode_splitkv_dv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                             int Dv, int num_splits);
+fmha_status fmha_decode_splitkv_dv(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                   int Dv, float scale, int causal, int num_splits,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace nvfp4_quantize needs (room for one fp32 amax).
  */
 size_t nvfp4_quantize_workspace_size(long long rows, int cols);

@@ -71,6 +71,43 @@ def test_decode_validation(kw, status):
     assert call_dec(**kw) == status
 
 
+def call_dec_dv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=1, Sq=1, Sk=1024, D=576,
+                Dv=512, scale=0.125, causal=0, ns=4, ws=None, wsb=0):
+    return F.load_library().fmha_decode_splitkv_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv,
+                                                   scale, causal, ns, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Dv=256), 3), (dict(D=512, Dv=576), 3), (dict(D=128, Dv=64), 3), (dict(Dv=576), 3),
+    (dict(D=64, Dv=512), 3),
+    (dict(k=None), 1), (dict(o=None), 1), (dict(Hq=6, Hkv=4), 4), (dict(v=FAKE + 2), 5),
+    (dict(ns=4, ws=None, wsb=0), 6), (dict(ns=4, ws=FAKE, wsb=1024), 6), (dict(ns=-1), 8),
+    (dict(Sq=2, Sk=1, causal=1), 2),
+])
+def test_decode_dv_validation(kw, status):
+    assert call_dec_dv(**kw) == status
+    assert F.load_library().fmha_last_error()
+
+
+def test_decode_576_needs_the_dv_entry_point():
+    assert call_dec(D=576) == 3
+    lib = F.load_library()
+    assert lib.fmha_decode_splitkv_nvfp4(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 1, 1024, 576,
+                                         0.125, 0, 1, None, 0, FAKE, FAKE, FAKE, None) == 3
+    assert call_paged(D=576) == 3
+
+
+def test_dv_workspace_formula():
+    rows, ns, dv = 32 * 64, 8, 512
+    want = -(-rows * ns * dv * 4 // 256) * 256 + -(-rows * ns * 4 // 256) * 256
+    assert F.fmha_decode_splitkv_dv_workspace_size(32, 64, 1, 1, 16384, 576, 512, 8) == want
+    assert F.fmha_decode_splitkv_dv_workspace_size(32, 64, 1, 1, 16384, 576, 576, 8) == 0
+    assert F.fmha_decode_splitkv_dv_workspace_size(32, 64, 1, 1, 16384, 576, 512, 1) == 0
+    # equal dims: the plain decode's formula
+    assert (F.fmha_decode_splitkv_dv_workspace_size(64, 32, 8, 1, 8192, 64, 64, 16) ==
+            F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 64, 16))
+
+
 def call_paged(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, Hq=4, Hkv=1, Sq=1, sl=FAKE, bt=FAKE,
                mp=8, ps=64, npages=16, D=64, scale=0.125, causal=0, ns=4, ws=None, wsb=0):
     return F.load_library().fmha_decode_paged(q, k, v, o, lse, B, Hq, Hkv, Sq, sl, bt, mp, ps,

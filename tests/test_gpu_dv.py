@@ -1,0 +1,95 @@
+"""GPU parity of the split-KV decode with a V/O head dim different from the
+Q/K head dim (fmha_decode_splitkv_dv: D = 576, Dv = 512) against the fp64 CPU
+oracle, through the C ABI.  V is either its own [B, Hkv, Sk, Dv] tensor or the
+very K buffer, which makes V the first Dv columns of each K row; the oracle
+always gets V as its own tensor."""
+import pytest
+import torch
+
+import decode_fmha_fwd_amd as F
+from gpu_helpers import assert_parity, oracle_rows, poison_like, require_gpu
+from workloads import WORKLOADS, default_scale, make_qkv, make_workload_inputs, sample_rows, v_of
+
+pytestmark = pytest.mark.gpu
+
+D, DV = 576, 512
+
+
+def run_decode_dv(q, k, v, dv, scale, causal, num_splits):
+    """v is k: the K buffer is passed for V too (V inside the K rows)."""
+    dev = require_gpu()
+    qd, kd = q.to(dev), k.to(dev)
+    vd = kd if v is k else v.to(dev)
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    o = torch.full((B, Hq, Sq, dv), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    nb = F.fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, d, dv, num_splits)
+    ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=dev)
+    F.fmha_decode_splitkv_dv(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, d, dv, scale, causal,
+                             num_splits, ws, nb)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Sk, causal, num_splits, v_in_k
+    (1, 64, 1, 1, 777, False, 4, True),
+    (1, 64, 1, 1, 300, False, 1, True),
+    (2, 32, 2, 1, 500, False, 3, True),
+    (1, 32, 1, 2, 400, True, 2, True),
+    (2, 16, 1, 1, 1, False, 1, True),      # one key
+    (1, 128, 1, 1, 2085, False, 0, True),  # two row blocks, heuristic splits, ragged tail
+    (1, 64, 1, 1, 777, False, 4, False),
+    (2, 32, 2, 1, 500, False, 1, False),
+    (1, 32, 1, 2, 400, True, 2, False),
+    (3, 8, 1, 1, 130, False, 2, False),    # 8 rows: a partly filled row block
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_decode_dv_small_shapes(case):
+    B, Hq, Hkv, Sq, Sk, causal, ns, v_in_k = case
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, DV, seed=sum(case[:6]) + 7, sigma=0.5)
+    scale = default_scale(D)
+    o, lse = run_decode_dv(q, k, k if v_in_k else v, DV, scale, causal, ns)
+    v_ref = v_of(k, DV) if v_in_k else v
+    o_ref, lse_ref = oracle_rows(q, k, v_ref, scale, causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=str(case))
+
+
+def test_decode_dv_uses_only_the_first_dv_columns():
+    """With V inside the K rows, the 64 key dims past Dv take part in the
+    scores but never in the output: changing them moves O only through P."""
+    B, Hq, Hkv, Sq, Sk = 1, 16, 1, 1, 96
+    q, k, _ = make_qkv(B, Hq, Hkv, Sq, Sk, D, DV, seed=21, sigma=0.5)
+    q[..., DV:] = 0  # the extra key dims then do not move the scores either
+    k2 = k.clone()
+    k2[..., DV:] = torch.randn(k2[..., DV:].shape, generator=torch.Generator().manual_seed(5)).to(
+        torch.bfloat16)
+    scale = default_scale(D)
+    o1, l1 = run_decode_dv(q, k, k, DV, scale, False, 2)
+    o2, l2 = run_decode_dv(q, k2, k2, DV, scale, False, 2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_dv_workload_sampled():
+    w = WORKLOADS["decode_mqa_d576_dv512_v_in_k"]
+    q, k, v = make_workload_inputs(w)
+    assert v is k
+    o, lse = run_decode_dv(q, k, k, w.Dv, w.scale, w.causal, w.num_splits)
+    rows = sample_rows(w.B * w.Hq * w.Sq, 64, seed=17)
+    o_ref, lse_ref = oracle_rows(q, k, v_of(k, w.Dv), w.scale, w.causal, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=w.name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_decode_dv_equal_dims_match_the_plain_decode():
+    """fmha_decode_splitkv_dv with Dv == D is fmha_decode_splitkv, bit for bit."""
+    B, Hq, Hkv, Sq, Sk, d = 2, 16, 4, 1, 700, 128
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, d, seed=3)
+    o1, l1 = run_decode_dv(q, k, v, d, default_scale(d), False, 3)
+    dev = require_gpu()
+    o2, l2 = F.decode(q.to(dev), k.to(dev), v.to(dev), num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

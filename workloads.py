@@ -22,7 +22,7 @@ import torch
 class Workload:
     name: str
     kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4",
-                         # "decode_nvfp4_fused", "decode_paged"
+                         # "decode_nvfp4_fused", "decode_paged", "decode_dv" (Dv != D)
     B: int
     Hq: int
     Hkv: int
@@ -106,6 +106,10 @@ WORKLOADS = {
                  v_is_k=True,
                  note="the wide-head decode with V the same tensor as K (a shared latent): "
                       "each key row is streamed once"),
+        Workload("decode_mqa_d576_dv512_v_in_k", "decode_dv", 32, 64, 1, 1, 16384, 576, 512, 0.5,
+                 5, False, v_is_k=True,
+                 note="the wide-head decode with Q/K head dim 576 and V the first 512 columns "
+                      "of each K row (a 512-wide latent plus 64 more key dims)"),
     ]
 }
 
@@ -158,8 +162,15 @@ def page_pool(k, v, lens, page_size, *, seed, spare_pages=2):
 
 
 def make_workload_inputs(w: Workload):
+    """(q, k, v); with v_is_k, v is k itself (V = the first Dv columns of each K row)."""
     q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, w.Dv, sigma=w.sigma, seed=w.seed)
     return (q, k, k) if w.v_is_k else (q, k, v)
+
+
+def v_of(k, dv):
+    """V as its own contiguous tensor when V is the first dv columns of the K
+    rows (for a caller that needs V apart, such as the oracle)."""
+    return k if k.shape[-1] == dv else k[..., :dv].contiguous()
 
 
 def sample_rows(total: int, n: int, seed: int = 1234) -> np.ndarray:
