@@ -9,6 +9,14 @@ decode workloads fmha_decode_splitkv (split kernel + log-sum-exp combine), or
 its paged, fused-NVFP4 and Dv != D variants; for the NVFP4 workload the decode
 with the amax folded in plus nvfp4_quantize.
 
+Before its W warm-up steps each workload runs untimed back-to-back steps for
+--settle-ms (default 60 ms): from idle the GPU clocks take ~15 ms of sustained
+load to settle, and the first few hundred prefill steps run up to 20% slower.
+`--trace-summary CSV` reads a rocprofv3 kernel trace of a bench run and
+prints, per workload, the durations of the timed dispatches only (the last
+--steps dispatches of each kernel; workloads are told apart by the seconds of
+input generation between them).
+
 The headline line is the causal prefill (B=4, H=16, S=2048, D=64) in TFLOP/s;
 the line also carries, under "workloads", every named workload (time per step,
 TFLOP/s, KV GB/s and fraction of the bound) and a "roofline" object for the
@@ -18,6 +26,7 @@ oracle timed on a bounded sample of the same workload ("cpu_baseline").
 from __future__ import annotations
 
 import argparse
+import csv
 import json
 import os
 import sys
@@ -36,13 +45,24 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed back-to-back steps for at least this long before the warm-up "
+                         "steps, so the GPU clocks have left their idle state (0 = none)")
     ap.add_argument("--workload", default="prefill_causal_d64")
     ap.add_argument("--only", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarise a rocprofv3 kernel_trace.csv of a bench run (timed "
+                         "dispatches of each workload) as a markdown table, then exit")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="HBM bytes per launch of --workload's kernels from rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run, scaled by the "
+                         "same counters of a --copy-calibration run, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), as the "
                          "reference reading for HBM byte counters, then exit")
@@ -137,9 +157,21 @@ class Runner:
             setattr(self, n, None)
 
 
-def time_workload(w, dev, steps, warmup):
+def settle(r, ms):
+    """Back-to-back steps for at least `ms` of wall time (GPU clocks ramp up
+    over ~15 ms of sustained load from idle)."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            r.step()
+        torch.cuda.synchronize()
+
+
+def time_workload(w, dev, steps, warmup, settle_ms=0.0):
     import torch
     r = Runner(w, dev)
+    settle(r, settle_ms)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -241,8 +273,85 @@ def cpu_baseline(w, target_s):
                       f"{dt:.1f} s wall"}
 
 
+def trace_summary(path, steps, names):
+    """Per workload (in run order) and kernel: count, average, min and max
+    duration of the last `steps` dispatches, from a rocprofv3 kernel trace."""
+    with open(path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    kn = "Kernel_Name" if "Kernel_Name" in rows[0] else "Kernel-Name"
+    recs = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r[kn]) for r in rows)
+    segs, cur, last_end = [], [], None
+    for st, en, k in recs:
+        if last_end is not None and st - last_end > 500_000_000:  # > 0.5 s idle: next workload
+            segs.append(cur)
+            cur = []
+        cur.append((st, en, k))
+        last_end = en if last_end is None else max(last_end, en)
+    segs.append(cur)
+    print("| workload | kernel | timed dispatches | average µs | min µs | max µs |")
+    print("|---|---|---|---|---|---|")
+    for i, seg in enumerate(segs):
+        wname = names[i] if i < len(names) else f"segment {i}"
+        per = {}
+        for st, en, k in seg:
+            per.setdefault(k, []).append((en - st) / 1e3)
+        for k, d in per.items():
+            if len(d) < steps:
+                continue  # set-up work, not a timed kernel
+            d = d[-steps:]
+            short = k if len(k) <= 110 else k[:107] + "..."
+            print(f"| {wname} | `{short}` | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                  f"{max(d):.2f} |")
+
+
+def _counter_kib(path):
+    """Kernel name -> mean counter value (KiB) per dispatch, from a rocprofv3
+    counter_collection.csv holding one counter."""
+    per = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def traffic_summary(w, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib_mib=1024):
+    """Markdown rows of read/written bytes per launch of each of the workload's
+    kernels, and the machine-readable line for the attention kernel."""
+    copy_bytes = calib_mib << 20
+    cf, cw = _counter_kib(cal_fetch_csv), _counter_kib(cal_write_csv)
+    kf = max(cf, key=cf.get)  # the copy kernel (largest reading)
+    f_scale = copy_bytes / (cf[kf] * 1024)
+    w_scale = copy_bytes / (cw[kf] * 1024)
+    fetch, write = _counter_kib(fetch_csv), _counter_kib(write_csv)
+    print(f"calibration: {kf}: FETCH_SIZE {cf[kf]:.0f} KiB, WRITE_SIZE {cw[kf]:.0f} KiB for "
+          f"{calib_mib} MiB; scales {f_scale:.4f} (read), {w_scale:.4f} (write)")
+    main_bytes = None
+    for k in fetch:
+        if k.startswith("void at::") or k.startswith("__amd"):
+            continue  # torch's own fills
+        rb = fetch[k] * 1024 * f_scale
+        wb = write.get(k, 0.0) * 1024 * w_scale
+        short = k if len(k) <= 80 else k[:77] + "..."
+        print(f"| {w.name} | `{short}` | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | "
+              f"{rb / 1e6:.2f} | {wb / 1e6:.2f} | {w.bytes() / 1e6:.2f} |")
+        if "attn_fwd_kernel" in k:
+            main_bytes = int(rb + wb)
+    if main_bytes is not None:
+        print(f"traffic_bytes_per_launch {w.name} {main_bytes} sha {kernel_source_sha()}")
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        from workloads import WORKLOADS
+        traffic_summary(WORKLOADS[args.workload], *args.traffic_summary)
+        return
+    if args.trace_summary:
+        from workloads import WORKLOADS
+        head = WORKLOADS[args.workload]
+        names = [head.name] + ([] if args.only else [n for n in WORKLOADS if n != head.name])
+        trace_summary(args.trace_summary, args.steps, names)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the split-KV "
               "decode and prefill shard over independent (batch, head) units with no exchange, "
@@ -272,9 +381,10 @@ def main():
     for n in names:
         w = WORKLOADS[n]
         steps = args.steps
-        ms, per, wall = time_workload(w, dev, steps, args.warmup)
+        ms, per, wall = time_workload(w, dev, steps, args.warmup, args.settle_ms)
         results[n] = (ms, per, summarise(w, ms))
         print(f"# {n}: {ms:.4f} ms/step  {results[n][2]}", file=sys.stderr, flush=True)
+        time.sleep(0.6)  # an idle gap that marks the workload boundary in a kernel trace
 
     ms, per, s = results[head.name]
     kernel_ms = sorted(per)[len(per) // 2]
