@@ -207,8 +207,14 @@ constexpr float kRescaleSlack = 8.0f;
 //
 // DV: head dim of V and O (D: of Q and K).  With a shared ring (KVS) V is the
 // first DV columns of each K row.
+//
+// GROUP (with SPLIT): a workgroup takes p.splits_per_wg consecutive splits of
+// its (batch, KV head).  Their key ranges are contiguous, so one copy stream
+// runs through all of them; at every split boundary the softmax state is
+// written out as that split's partial and reset, which is the arithmetic of
+// one workgroup per split, without a short-lived workgroup per split.
 template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT,
-          bool KVS = false, bool PAGED = false, int DV = D>
+          bool KVS = false, bool PAGED = false, int DV = D, bool GROUP = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
@@ -232,6 +238,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   static_assert(!KVS || KST == VST, "a shared K/V ring has one depth");
   static_assert(DV <= D || !KVS, "V inside the K rows needs DV <= D");
   static_assert(DV == D || MT == 16, "separate V width: 16-row (decode) waves");
+  static_assert(!GROUP || SPLIT, "split groups write split partials");
   static_assert(!(KVS && PAGED), "a paged cache keeps K and V apart");
   static_assert(KT % MT == 0, "KT must be a multiple of MT");
   static_assert(MT == 32 || KT == 16 || KT % 32 == 0, "16-row waves: 16 keys or whole 32s");
@@ -257,12 +264,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   // count is a multiple of 8 in the usual shapes, all row blocks of one head
   // land on the same XCD (blocks go round-robin over the 8 XCDs) and share its
   // L2 for their K/V re-reads.
-  const int n_units = p.nsplit * p.Hkv * p.B;
+  const int spw = GROUP ? p.splits_per_wg : 1;     // splits per workgroup
+  const int nsg = (p.nsplit + spw - 1) / spw;        // split groups per (b, KV head)
+  const int n_units = nsg * p.Hkv * p.B;
   const int rb_rank = blockIdx.x / n_units;
   const int unit = blockIdx.x - rb_rank * n_units;
   const int rb = CAUSAL ? p.n_row_blocks - 1 - rb_rank : rb_rank;
-  const int split = unit % p.nsplit;
-  const int bk = unit / p.nsplit;
+  const int split0 = (unit % nsg) * spw;             // first split of this workgroup
+  const int nspl = min(spw, p.nsplit - split0);      // its splits
+  const int bk = unit / nsg;
   const int kvh = bk % p.Hkv;
   const int b = bk / p.Hkv;
 
@@ -281,9 +291,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const int my_rc = row_ok ? my_r : p.rows_per_kv - 1;
   const int diag = Sk - p.Sq;  // causal: key j visible to row i iff j <= i + diag
 
-  // Key range of this workgroup.
-  const int kbeg = split * p.split_len;
-  int kend = min(Sk, kbeg + p.split_len);
+  // Key range of this workgroup (its splits, back to back).
+  const int kbeg = split0 * p.split_len;
+  int kend = min(Sk, kbeg + nspl * p.split_len);
   int wave_min_last = INT_MAX;  // smallest last-visible key over the wave's rows
   int wave_max_last = INT_MAX;  // largest
   if (CAUSAL) {
@@ -627,14 +637,66 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     });
   };
 
+  // The split-s partial of this workgroup's rows: fp32 O / l and its lse.
+  auto write_partial = [&](int s) {
+    const float l_tot = group_sum<MT>(l_run);
+    const bool empty = !(l_tot > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / l_tot;
+    const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
+    if (row_ok) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+        for (int qd = 0; qd < M::kRegs / 4; ++qd) {
+          const int d0 = (MT == 32) ? db * 32 + 8 * qd + 4 * kg : db * 16 + 4 * kg;
+          if (d0 >= DV) continue;
+          float* dst = p.o_part + ((row_base + my_r) * p.nsplit + s) * DV + d0;
+          *(f32x4*)dst = f32x4{oacc[db][4 * qd + 0] * inv, oacc[db][4 * qd + 1] * inv,
+                               oacc[db][4 * qd + 2] * inv, oacc[db][4 * qd + 3] * inv};
+        }
+      }
+      if (kg == 0) p.lse_part[(row_base + my_r) * p.nsplit + s] = lse_val;
+    }
+  };
+  auto reset_state = [&]() {
+    m_run = kNegBig;
+    l_run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) oacc[i] = Acc{};
+  };
+  const int tps = p.split_len / KT;  // tiles per split
+  int s_done = 0;                    // splits of the group written so far
   for (int it0 = 0; it0 < ntiles; it0 += LCM) {
     static_for<0, LCM>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
-      if (it0 + U < ntiles) tile(u_c, it0 + U);
+      const int it = it0 + U;
+      if (it < ntiles) {
+        tile(u_c, it);
+        if constexpr (GROUP) {
+          if ((it + 1) % tps == 0 && it + 1 < ntiles) {  // the last tile of a split
+            write_partial(split0 + s_done);
+            ++s_done;
+            reset_state();
+          }
+        }
+      }
     });
   }
 
   // ---- epilogue: O / l, log-sum-exp ----
+  if constexpr (SPLIT) {
+    if constexpr (GROUP) {
+      // the split holding the last tile, then any later split of the group
+      // with no visible key (lse = -inf, O = 0)
+      for (int j = s_done; j < nspl; ++j) {
+        write_partial(split0 + j);
+        reset_state();
+      }
+    } else {
+      write_partial(split0);
+    }
+    return;
+  }
   const float l_tot = group_sum<MT>(l_run);
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
@@ -650,34 +712,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         if (d0 >= DV) continue;
         const float o0 = oacc[db][4 * qd + 0] * inv, o1 = oacc[db][4 * qd + 1] * inv;
         const float o2 = oacc[db][4 * qd + 2] * inv, o3 = oacc[db][4 * qd + 3] * inv;
-        if constexpr (SPLIT) {
-          float* dst = p.o_part + ((row_base + my_r) * p.nsplit + split) * DV + d0;
-          *(f32x4*)dst = f32x4{o0, o1, o2, o3};
-        } else {
-          const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
-          if (p.o) *(u32x2*)(p.o + (row_base + my_r) * DV + d0) = u32x2{w0, w1};
-          if (p.o_amax) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 >> 16)));
-          }
+        const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
+        if (p.o) *(u32x2*)(p.o + (row_base + my_r) * DV + d0) = u32x2{w0, w1};
+        if (p.o_amax) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 >> 16)));
         }
       }
     }
-    if (kg == 0) {
-      if constexpr (SPLIT) {
-        p.lse_part[(row_base + my_r) * p.nsplit + split] = lse_val;
-      } else if (p.lse) {
-        p.lse[row_base + my_r] = lse_val;
-      }
-    }
+    if (kg == 0 && p.lse) p.lse[row_base + my_r] = lse_val;
   }
-  if constexpr (!SPLIT) {
-    if (p.o_amax) {
-      amax = wave_max(amax);
-      if (lane == 0) atomic_max_nonneg(p.o_amax, amax);
-    }
+  if (p.o_amax) {
+    amax = wave_max(amax);
+    if (lane == 0) atomic_max_nonneg(p.o_amax, amax);
   }
 
   // Fused NVFP4 output (16-row waves): the 16-element block of head dims

@@ -23,10 +23,15 @@ fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 
   // V aliasing K at head dim 512: one 5-deep ring of 32-key tiles (160 KB)
   if (D == 512 && kv_shared)
     return launch_attn_cs<512, 16, 4, 32, 5, 5, true>(p, grid, causal, split, st);
-  if (D == 64 && c.nw == 1) return launch_attn_cs<64, 16, 1, 32, 3, 3>(p, grid, causal, split, st);
-  if (D == 64 && c.nw == 4) return launch_attn_cs<64, 16, 4, 64, 3, 3>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 1) return launch_attn_cs<128, 16, 1, 32, 2, 2>(p, grid, causal, split, st);
-  if (D == 128 && c.nw == 4) return launch_attn_cs<128, 16, 4, 64, 2, 2>(p, grid, causal, split, st);
+  // (head dims 64 and 128 also come with split groups; see decode_groups_built)
+  if (D == 64 && c.nw == 1)
+    return launch_attn_cs<64, 16, 1, 32, 3, 3, false, false, 64, true>(p, grid, causal, split, st);
+  if (D == 64 && c.nw == 4)
+    return launch_attn_cs<64, 16, 4, 64, 3, 3, false, false, 64, true>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 1)
+    return launch_attn_cs<128, 16, 1, 32, 2, 2, false, false, 128, true>(p, grid, causal, split, st);
+  if (D == 128 && c.nw == 4)
+    return launch_attn_cs<128, 16, 4, 64, 2, 2, false, false, 128, true>(p, grid, causal, split, st);
   if (D == 512) return launch_attn_cs<512, 16, 4, 32, 3, 2>(p, grid, causal, split, st);
   return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv: head dim %d not built", D);
 }

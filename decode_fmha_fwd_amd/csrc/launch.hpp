@@ -29,6 +29,7 @@ struct AttnParams {
   int n_row_blocks;     // ceil(rows_per_kv / (NW * MT))
   int nsplit;           // key ranges per (batch, KV head)
   int split_len;        // keys per range, a multiple of KT
+  int splits_per_wg;    // consecutive splits one workgroup takes (split groups), >= 1
   float scale_log2;     // scale * log2(e)
   // Paged KV cache (decode only).  K and V are [num_pages][Hkv][page_size][D];
   // key j of batch b sits in page block_table[b * bt_stride + j / page_size].
@@ -55,6 +56,13 @@ inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
   if (D >= 512) return {4, 32, 1};
   if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 5};
   return {4, 64, D == 64 ? 3 : 2};
+}
+
+// Decode configurations built with split groups (one workgroup streaming
+// several consecutive splits): head dims 64 and 128, two separate rings, a
+// contiguous cache.
+inline bool decode_groups_built(int D, int Dv, bool kv_shared) {
+  return Dv == D && (D == 64 || D == 128) && !kv_shared;
 }
 
 // fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).

@@ -227,3 +227,23 @@ def test_decode_amax_fold():
         amax = torch.zeros(1, dtype=torch.float32, device=dev)
         o, _ = run_decode(q, k, v, default_scale(128), False, ns, o_amax=amax)
         assert amax.item() == o.float().abs().max().item()
+
+
+@pytest.mark.parametrize("D,Sq,causal", [(64, 1, False), (64, 2, True), (128, 1, False)])
+def test_split_groups_equal_one_workgroup_per_split(D, Sq, causal):
+    """When the (batch, KV head) units alone give every CU two or more
+    workgroups (here 64 x 8 = 512 units), one workgroup streams all splits of
+    its unit and writes each split's partial: the arithmetic of one workgroup
+    per split.  Batches of the grouped run must equal single-batch runs (8
+    units, not grouped) bit for bit, and the oracle."""
+    B, Hq, Hkv, Sk, ns = 64, 32, 8, 1000, 8   # 8 splits of 128 keys, the last ragged
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=D + Sq)
+    scale = default_scale(D)
+    o, lse = run_decode(q, k, v, scale, causal, ns)
+    for b in (0, 17, 63):
+        o1, l1 = run_decode(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale, causal, ns)
+        assert torch.equal(o[b].view(torch.int16), o1[0].view(torch.int16)), b
+        assert torch.equal(lse[b], l1[0]), b
+    rows = sample_rows(B * Hq * Sq, 64, seed=29)
+    o_ref, lse_ref = oracle_rows(q, k, v, scale, causal, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=f"D={D} Sq={Sq} grouped splits")

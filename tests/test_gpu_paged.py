@@ -105,3 +105,23 @@ def test_paged_gqa_decode_workload_equals_contiguous():
     del kc, vc
     o2, l2 = run_contiguous(q, k, v, w.scale, w.causal, w.num_splits)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_paged_split_groups_with_empty_splits():
+    # 64 batches x 8 KV heads x 16 splits, lengths from 0 to 2048: whole
+    # splits without keys (lse -inf, O 0 in the partials) next to full ones
+    B, Hq, Hkv, D, P, ns = 64, 8, 8, 64, 64, 16
+    lens = [int(x) for x in np.random.default_rng(3).integers(0, 2049, size=B)]
+    lens[0], lens[1] = 0, 2048
+    q, k, v = make_qkv(B, Hq, Hkv, 1, 2048, D, seed=19)
+    kc, vc, table, num_pages = page_pool(k, v, lens, P, seed=23)
+    scale = default_scale(D)
+    o, lse = run_paged(q, kc, vc, lens, table, P, num_pages, scale, False, ns)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(o[b].float().cpu(), torch.zeros(Hq, 1, D))
+            assert torch.isinf(lse[b]).all() and (lse[b] < 0).all()
+            continue
+        o_ref, lse_ref = oracle_rows(q[b:b + 1], k[b:b + 1, :, :n].contiguous(),
+                                     v[b:b + 1, :, :n].contiguous(), scale, False)
+        assert_parity(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, what=f"batch {b} ({n} keys)")
