@@ -87,9 +87,10 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  * Split-KV decode (small Sq, e.g. 1): the keys of each (batch, KV head) are cut
  * into num_splits contiguous ranges (equal lengths rounded up to the KV tile;
  * trailing splits may be empty).  One workgroup handles all query rows that
- * share a KV head (the Hq/Hkv grouped heads times Sq) over one range and writes
- * an fp32 partial output and its log-sum-exp to the workspace; a second kernel
- * combines them:  LSE = m + log sum_s exp(lse_s - m),  m = max_s lse_s,
+ * share a KV head (the Hq/Hkv grouped heads times Sq) over one range, or over
+ * all ranges of its (batch, KV head) back to back when those units alone fill
+ * the GPU, and writes an fp32 partial output and its log-sum-exp per range to
+ * the workspace; a second kernel combines them:  LSE = m + log sum_s exp(lse_s - m),  m = max_s lse_s,
  * O = sum_s exp(lse_s - LSE) * O_s.   With one split the first kernel writes
  * O and LSE directly and no workspace is used.
  *   D in {64, 128, 512}; the Sq*Hq/Hkv rows of a KV head are taken in

@@ -1,0 +1,71 @@
+"""Host logic of bench.py (no GPU): the rocprofv3 trace and counter summaries
+that the profiles are made from, and the algorithmic work of the workloads."""
+import csv
+
+import pytest
+
+import bench
+from workloads import WORKLOADS
+
+
+def _write(path, fields, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_trace_summary_takes_the_last_steps_of_each_workload(tmp_path, capsys):
+    # two workloads separated by a 2 s gap; the first runs 5 untimed launches
+    # of 100 us, then 3 timed ones of 40 us
+    rows, t = [], 0
+    for dur in [100] * 5 + [40] * 3:
+        rows.append({"Kernel_Name": "attnA", "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+        t += 200_000
+    t += 2_000_000_000
+    for dur in [7, 7, 9, 9, 9]:
+        for k in ("attnB", "combine"):
+            rows.append({"Kernel_Name": k, "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+            t += 50_000
+    p = tmp_path / "trace.csv"
+    _write(p, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    bench.trace_summary(str(p), 3, ["first", "second"])
+    out = capsys.readouterr().out.splitlines()
+    body = [ln for ln in out if ln.startswith("| first") or ln.startswith("| second")]
+    assert len(body) == 3
+    assert "`attnA` | 3 | 40.00 | 40.00 | 40.00" in body[0]
+    assert "`attnB` | 3 | 9.00 |" in body[1] and "`combine` | 3 | 9.00 |" in body[2]
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, capsys):
+    fields = ["Kernel_Name", "Counter_Value"]
+    # a 1 MiB copy read as 512 KiB by FETCH_SIZE and 1024 KiB by WRITE_SIZE
+    _write(tmp_path / "cf.csv", fields, [{"Kernel_Name": "__amd_copy", "Counter_Value": 512}])
+    _write(tmp_path / "cw.csv", fields, [{"Kernel_Name": "__amd_copy", "Counter_Value": 1024}])
+    _write(tmp_path / "f.csv", fields, [
+        {"Kernel_Name": "void fmha::attn_fwd_kernel<64>(p)", "Counter_Value": 1000},
+        {"Kernel_Name": "void fmha::attn_fwd_kernel<64>(p)", "Counter_Value": 3000},
+        {"Kernel_Name": "void at::native::fill(x)", "Counter_Value": 5}])
+    _write(tmp_path / "w.csv", fields, [
+        {"Kernel_Name": "void fmha::attn_fwd_kernel<64>(p)", "Counter_Value": 10}])
+    w = WORKLOADS["decode_gqa_d64"]
+    bench.traffic_summary(w, str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                          str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), calib_mib=1)
+    out = capsys.readouterr().out
+    # mean FETCH 2000 KiB x 2 (scale) + WRITE 10 KiB x 1
+    line = [ln for ln in out.splitlines() if ln.startswith("traffic_bytes_per_launch")][0]
+    assert line.split()[1] == w.name and int(line.split()[2]) == 2000 * 1024 * 2 + 10 * 1024
+    assert "at::native" not in out
+
+
+@pytest.mark.parametrize("name,flops,nbytes", [
+    # 4 * B * Hq * D * visible pairs; Q, K, V read once, O and LSE written once
+    ("single_tile_d16", 4 * 16 * 128 * 128, 2 * (3 * 128 * 16 + 128 * 16) + 4 * 128),
+    ("decode_gqa_d64", 4 * 64 * 32 * 64 * 8192,
+     2 * (64 * 32 * 64 + 2 * 64 * 8 * 8192 * 64 + 64 * 32 * 64) + 4 * 64 * 32),
+    ("decode_mqa_d576_dv512_v_in_k", 2 * (576 + 512) * 32 * 64 * 16384,
+     2 * (32 * 64 * 576 + 32 * 16384 * 576 + 32 * 64 * 512) + 4 * 32 * 64),
+])
+def test_workload_algorithmic_counts(name, flops, nbytes):
+    w = WORKLOADS[name]
+    assert w.flops() == flops and w.bytes() == nbytes
