@@ -88,7 +88,7 @@ FWD_CASES = [
     (3, 3, 1, 45, 45, 128, True),
     (1, 2, 1, 300, 100, 64, False),     # more queries than keys
     (2, 6, 3, 129, 129, 32, True),      # odd group size, one row past a 128-row block
-    # head dim 64 (256-row workgroups of two alternating wave groups)
+    # head dim 64: several 128-row blocks, long key ranges
     (1, 2, 2, 600, 600, 64, True),      # three row blocks, the last ragged
     (2, 2, 2, 512, 512, 64, True),      # whole row blocks
     (1, 8, 2, 100, 100, 64, True),      # GQA: one row block spans four heads
@@ -229,21 +229,26 @@ def test_decode_amax_fold():
         assert amax.item() == o.float().abs().max().item()
 
 
-@pytest.mark.parametrize("D,Sq,causal", [(64, 1, False), (64, 2, True), (128, 1, False)])
-def test_split_groups_equal_one_workgroup_per_split(D, Sq, causal):
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,D,causal,ns", [
+    (64, 32, 8, 1, 1000, 64, False, 8),    # 1-wave workgroups, 8 splits of 128 keys, last ragged
+    (64, 32, 8, 2, 1000, 64, True, 8),     # causal, two query rows
+    (64, 32, 8, 1, 1000, 128, False, 8),
+    (256, 64, 2, 1, 300, 64, False, 4),    # 32 rows per KV head: 4-wave workgroups
+    (256, 64, 2, 1, 300, 128, False, 3),
+])
+def test_split_groups_equal_one_workgroup_per_split(B, Hq, Hkv, Sq, Sk, D, causal, ns):
     """When the (batch, KV head) units alone give every CU two or more
-    workgroups (here 64 x 8 = 512 units), one workgroup streams all splits of
-    its unit and writes each split's partial: the arithmetic of one workgroup
-    per split.  Batches of the grouped run must equal single-batch runs (8
-    units, not grouped) bit for bit, and the oracle."""
-    B, Hq, Hkv, Sk, ns = 64, 32, 8, 1000, 8   # 8 splits of 128 keys, the last ragged
-    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=D + Sq)
+    workgroups (here 512 units), one workgroup streams all splits of its unit
+    and writes each split's partial: the arithmetic of one workgroup per
+    split.  Batches of the grouped run must equal single-batch runs (too few
+    units to group) bit for bit, and the oracle."""
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=D + Sq + B)
     scale = default_scale(D)
     o, lse = run_decode(q, k, v, scale, causal, ns)
-    for b in (0, 17, 63):
+    for b in (0, B // 3, B - 1):
         o1, l1 = run_decode(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale, causal, ns)
         assert torch.equal(o[b].view(torch.int16), o1[0].view(torch.int16)), b
         assert torch.equal(lse[b], l1[0]), b
     rows = sample_rows(B * Hq * Sq, 64, seed=29)
     o_ref, lse_ref = oracle_rows(q, k, v, scale, causal, rows=rows)
-    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=f"D={D} Sq={Sq} grouped splits")
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=f"B={B} D={D} grouped splits")
