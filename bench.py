@@ -72,14 +72,15 @@ def parse():
 class Runner:
     """Device buffers and the step function of one workload."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, inputs=None):
         import torch
 
         import decode_fmha_fwd_amd as F
         from workloads import make_workload_inputs, page_pool
 
         self.w, self.F, self.torch = w, F, torch
-        q, k, v = make_workload_inputs(w)
+        q, k, v = inputs if inputs is not None else make_workload_inputs(w)
+        inputs = None
         self.q = q.to(dev)
         if w.kind == "decode_paged":
             # the same K/V as a paged cache in shuffled page order
@@ -190,9 +191,9 @@ def settle(r, ms):
         torch.cuda.synchronize()
 
 
-def time_workload(w, dev, steps, warmup, settle_ms=0.0):
+def time_workload(w, dev, steps, warmup, settle_ms=0.0, inputs=None):
     import torch
-    r = Runner(w, dev)
+    r = Runner(w, dev, inputs)
     settle(r, settle_ms)
     for _ in range(warmup):
         r.step()
@@ -282,7 +283,7 @@ def cpu_baseline(w, target_s):
         rows = sample_rows(total, n, seed=99)
         t0 = time.perf_counter()
         oracle.attention(qa, ka, va, B=w.B, Hq=w.Hq, Hkv=w.Hkv, Sq=w.Sq, Sk=w.Sk, D=w.D, Dv=w.Dv,
-                         scale=w.scale, causal=w.causal, rows=rows)
+                         scale=w.scale, causal=w.causal, rows=rows, nthreads=all_threads())
         dt = time.perf_counter() - t0
         flops = float(2 * (w.D + w.Dv) * vis(rows).sum())
         return rows.size, dt, flops
@@ -291,7 +292,7 @@ def cpu_baseline(w, target_s):
     n2 = int(min(total, max(64, n * target_s / max(dt, 1e-3))))
     if n2 > n:
         n, dt, fl = run(n2)
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": all_threads(),
             "kind": "oracle",
             "sample": f"{n} of {total} query rows of {w.name} (seeded sample), fp64, "
                       f"{dt:.1f} s wall"}
@@ -364,6 +365,85 @@ def traffic_summary(w, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib
         print(f"traffic_bytes_per_launch {w.name} {main_bytes} sha {kernel_source_sha()}")
 
 
+def _bits(t):
+    import numpy as np
+    import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_ALL_THREADS = []
+
+
+def all_threads() -> int:
+    """The oracle's default OpenMP thread count, read before any call sets it
+    (a call with an explicit count changes it for later calls)."""
+    if not _ALL_THREADS:
+        import oracle
+        _ALL_THREADS.append(oracle.num_threads())
+    return _ALL_THREADS[0]
+
+
+def _rows(total, n):
+    import numpy as np
+
+    from workloads import sample_rows
+    return np.arange(total, dtype=np.int64) if n >= total else sample_rows(total, n, seed=99)
+
+
+def cpu_sample(w, q, k, v, target_s, threads=0):
+    """The fp64 oracle beside one workload: a seeded sample of its query rows
+    sized to about target_s of wall time (all host threads unless `threads`),
+    as TFLOP/s of the same algorithmic count."""
+    import numpy as np
+
+    import oracle
+    from workloads import v_of
+
+    threads = threads or all_threads()
+    qa, ka, va = _bits(q), _bits(k), _bits(v_of(v, w.Dv))
+    total = w.B * w.Hq * w.Sq
+
+    def run(n):
+        rows = _rows(total, n)
+        t0 = time.perf_counter()
+        oracle.attention(qa, ka, va, B=w.B, Hq=w.Hq, Hkv=w.Hkv, Sq=w.Sq, Sk=w.Sk, D=w.D,
+                         Dv=w.Dv, scale=w.scale, causal=w.causal, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        i = rows % w.Sq
+        vis = (np.full(rows.shape, w.Sk, dtype=np.int64) if not w.causal
+               else np.minimum(w.Sk, i + 1 + w.Sk - w.Sq))
+        return rows.size, dt, float(2 * (w.D + w.Dv) * vis.sum())
+
+    n, dt, fl = run(8)
+    n2 = int(min(total, max(8, n * target_s / max(dt, 1e-4))))
+    if n2 > n:
+        n, dt, fl = run(n2)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "rows": n, "of_rows": total,
+            "seconds": round(dt, 5), "threads": threads}
+
+
+def cpu_nvfp4_sample(x, cols):
+    """The oracle's fp32 step-by-step NVFP4 quantiser on a bf16 tensor of the
+    output's shape (one host thread), in seconds."""
+    import oracle
+    xa = _bits(x)
+    rows = xa.size // cols
+    t0 = time.perf_counter()
+    oracle.nvfp4_quantize(xa, rows, cols)
+    return {"seconds": round(time.perf_counter() - t0, 5), "elements": int(xa.size)}
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -402,11 +482,26 @@ def main():
     head = WORKLOADS[args.workload]
     names = [head.name] + ([] if args.only else [n for n in WORKLOADS if n != head.name])
     results = {}
+    from workloads import make_workload_inputs
+    if not args.no_cpu_baseline:
+        all_threads()  # before any single-thread oracle call
     for n in names:
         w = WORKLOADS[n]
         steps = args.steps
-        ms, wall = time_workload(w, dev, steps, args.warmup, args.settle_ms)
+        inputs = make_workload_inputs(w)
+        oracle_beside = None
+        if not args.no_cpu_baseline:
+            # the oracle on a bounded sample of this workload's own inputs
+            oracle_beside = cpu_sample(w, *inputs, target_s=1.0)
+            if w.name == "single_tile_d16":  # the whole tile, one host thread
+                oracle_beside["one_thread"] = cpu_sample(w, *inputs, target_s=1.0, threads=1)
+            if w.kind.startswith("decode_nvfp4"):
+                oracle_beside["nvfp4_quantize"] = cpu_nvfp4_sample(inputs[0], w.Dv)
+        ms, wall = time_workload(w, dev, steps, args.warmup, args.settle_ms, inputs)
+        del inputs
         results[n] = (ms, summarise(w, ms))
+        if oracle_beside is not None:
+            results[n][1]["cpu_oracle"] = oracle_beside
         print(f"# {n}: {ms:.4f} ms/step  {results[n][1]}", file=sys.stderr, flush=True)
         time.sleep(0.6)  # an idle gap that marks the workload boundary in a kernel trace
 
@@ -430,6 +525,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head, args.cpu_seconds)
+        cpu["cpu_model"] = cpu_model()
 
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
