@@ -99,7 +99,7 @@ class Runner:
         self.lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
         self.ws = None
         self.ws_bytes = 0
-        if w.kind != "fwd":
+        if not w.kind.startswith("fwd"):
             self.ws_bytes = F.fmha_decode_splitkv_dv_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk,
                                                                     w.D, w.Dv, w.num_splits)
             if self.ws_bytes:
@@ -137,6 +137,10 @@ class Runner:
             a = (P(self.q), P(self.k), P(self.v), P(self.o), P(self.lse), w.B, w.Hq, w.Hkv, w.Sq,
                  w.Sk, w.D, float(w.scale), int(w.causal), st)
             self.bound = ("fmha_fwd", lib.fmha_fwd, a)
+        elif w.kind == "fwd_dv":
+            a = (P(self.q), P(self.k), P(self.v), P(self.o), P(self.lse), w.B, w.Hq, w.Hkv, w.Sq,
+                 w.Sk, w.D, w.Dv, float(w.scale), int(w.causal), st)
+            self.bound = ("fmha_fwd_dv", lib.fmha_fwd_dv, a)
         elif w.kind == "decode":
             a = (P(self.q), P(self.k), P(self.v), P(self.o), P(self.lse), w.B, w.Hq, w.Hkv, w.Sq,
                  w.Sk, w.D, float(w.scale), int(w.causal), w.num_splits, P(self.ws),
@@ -250,7 +254,7 @@ def summarise(w, ms):
            "tflops": round(w.flops() / s / 1e12, 2),
            "kv_gbs": round(kv / s / 1e9, 1),
            "alg_gbs": round(w.bytes() / s / 1e9, 1)}
-    if w.kind == "fwd" and w.Sq > 1:
+    if w.kind.startswith("fwd") and w.Sq > 1:
         out["bound"] = "mfma"
         out["frac_of_bound"] = round(out["tflops"] / BF16_PEAK_TFLOPS, 4)
     else:
@@ -507,12 +511,14 @@ def main():
 
     ms, s = results[head.name]
     kernel_ms = ms  # one kernel per prefill step: its mean launch duration
-    if head.kind == "fwd":
+    if head.kind.startswith("fwd"):
         achieved = head.flops() / (kernel_ms / 1e3) / 1e12
+        kname = (f"attn_fwd_kernel<{head.D},32,4,64,{'causal' if head.causal else 'non-causal'}"
+                 + (f",Dv={head.Dv}>" if head.Dv != head.D else ">"))
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(head.name),
-                "kernel": "attn_fwd_kernel<64,32,4,64,causal>", "kernel_ms_mean": round(kernel_ms, 5)}
+                "kernel": kname, "kernel_ms_mean": round(kernel_ms, 5)}
         value, unit = s["tflops"], "TFLOP/s"
     else:
         achieved = head.bytes() / (kernel_ms / 1e3) / 1e9

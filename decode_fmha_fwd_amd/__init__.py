@@ -31,6 +31,7 @@ STATUS = {0: "FMHA_OK", 1: "FMHA_ERR_NULL", 2: "FMHA_ERR_SHAPE", 3: "FMHA_ERR_HE
 _P, _I, _LL, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fmha_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fmha_fwd_dv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fmha_decode_splitkv_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "fmha_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _SZ,
                                  _P, _P]),
@@ -105,6 +106,13 @@ def fmha_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, stream=None)
     st = stream if stream is not None else _stream(q.device)
     _check("fmha_fwd", lib.fmha_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                     Sq, Sk, D, float(scale), int(causal), st))
+
+
+def fmha_fwd_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, stream=None):
+    lib = load_library()
+    st = stream if stream is not None else _stream(q.device)
+    _check("fmha_fwd_dv", lib.fmha_fwd_dv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                          Hkv, Sq, Sk, D, Dv, float(scale), int(causal), st))
 
 
 def fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, num_splits) -> int:
@@ -188,15 +196,20 @@ def fmha_debug_qk_scores(q, k, s_out, Sq, Sk, D, scale, stream=None):
 # ---------------------------------------------------------------- conveniences
 
 def fwd(q, k, v, *, causal=False, scale=None, want_lse=True):
-    """Attention forward on [B, H, S, D] bf16 GPU tensors -> (o bf16, lse fp32 or None)."""
+    """Attention forward on [B, H, S, D] bf16 GPU tensors (V may have its own
+    head dim) -> (o bf16 [B, Hq, Sq, Dv], lse fp32 or None)."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_gpu_bf16(n, t)
     B, Hq, Sq, D = q.shape
     _, Hkv, Sk, _ = k.shape
+    Dv = v.shape[-1]
     scale = (1.0 / D ** 0.5) if scale is None else scale
-    o = torch.empty_like(q)
+    o = torch.empty((B, Hq, Sq, Dv), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if want_lse else None
-    fmha_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal)
+    if Dv == D:
+        fmha_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal)
+    else:
+        fmha_fwd_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal)
     return o, lse
 
 

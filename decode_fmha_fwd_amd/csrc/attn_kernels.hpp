@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   constexpr int kPerTile = nK + nV;
   static_assert(!KVS || KST == VST, "a shared K/V ring has one depth");
   static_assert(DV <= D || !KVS, "V inside the K rows needs DV <= D");
-  static_assert(DV == D || MT == 16, "separate V width: 16-row (decode) waves");
+  static_assert(DV == D || DV % MT == 0, "a separate V width in whole MT-wide blocks");
   static_assert(!GROUP || SPLIT, "split groups write split partials");
   static_assert(!(KVS && PAGED), "a paged cache keeps K and V apart");
   static_assert(KT % MT == 0, "KT must be a multiple of MT");

@@ -124,15 +124,25 @@ const char* fmha_status_string(fmha_status s) {
 
 const char* fmha_last_error(void) { return g_last_error; }
 
-fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+}  // extern "C"
+
+namespace {
+
+// (Q/K head dim, V/O head dim) pairs the prefill kernels are built for.
+bool fwd_dims_ok(int D, int Dv) { return (Dv == D && fwd_dim_ok(D)) || (D == 192 && Dv == 128); }
+
+fmha_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale, int causal,
                      void* stream) {
-  g_last_error[0] = 0;
   fmha_status s = check_common(q, k, v, o, B, Hq, Hkv, Sq, Sk, scale, causal);
   if (s != FMHA_OK) return s;
   if (lse && !aligned16(lse)) return fail(FMHA_ERR_ALIGN, "lse must be 16-byte aligned");
-  if (!fwd_dim_ok(D)) return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd supports D in {16,32,64,128}, got %d", D);
-  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D)) return fail(FMHA_ERR_SHAPE, "tensor too large");
+  if (!fwd_dims_ok(D, Dv))
+    return fail(FMHA_ERR_HEAD_DIM,
+                "prefill supports D = Dv in {16,32,64,128} and (D, Dv) = (192, 128), got (%d, %d)",
+                D, Dv);
+  if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D > Dv ? D : Dv))
+    return fail(FMHA_ERR_SHAPE, "tensor too large");
   AttnParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -151,7 +161,26 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.scale_log2 = scale * kLog2e;
   if (!grid_fits(p.n_row_blocks, 1, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
   dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
-  return launch_fwd(D, p, grid, causal != 0, (hipStream_t)stream);
+  return launch_fwd(D, Dv, p, grid, causal != 0, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+                     void* stream) {
+  g_last_error[0] = 0;
+  if (D == 192) return fail(FMHA_ERR_HEAD_DIM, "D = 192 needs Dv: use fmha_fwd_dv");
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, D, scale, causal, stream);
+}
+
+fmha_status fmha_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale, int causal,
+                        void* stream) {
+  g_last_error[0] = 0;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, stream);
 }
 
 int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D) {

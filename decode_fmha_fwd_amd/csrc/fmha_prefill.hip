@@ -10,33 +10,33 @@
 namespace fmha {
 namespace {
 
-template <int D, int MT, int NW, int KT, int KS, int VS, bool C, bool S>
+template <int D, int MT, int NW, int KT, int KS, int VS, bool C, int DV>
 fmha_status launch_attn(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, S>), grid, dim3(NW * 64), 0, st,
-                     p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, MT, NW, KT, KS, VS, C, false, false, false, DV>), grid,
+                     dim3(NW * 64), 0, st, p);
   return check_launch("attention kernel launch");
 }
 
-template <int D, int MT, int NW, int KT, int KS, int VS>
-fmha_status launch_attn_cs(const AttnParams& p, dim3 grid, bool causal, bool split,
-                           hipStream_t st) {
-  if (causal)
-    return split ? launch_attn<D, MT, NW, KT, KS, VS, true, true>(p, grid, st)
-                 : launch_attn<D, MT, NW, KT, KS, VS, true, false>(p, grid, st);
-  return split ? launch_attn<D, MT, NW, KT, KS, VS, false, true>(p, grid, st)
-               : launch_attn<D, MT, NW, KT, KS, VS, false, false>(p, grid, st);
+template <int D, int MT, int NW, int KT, int KS, int VS, int DV = D>
+fmha_status launch_attn_c(const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
+  return causal ? launch_attn<D, MT, NW, KT, KS, VS, true, DV>(p, grid, st)
+                : launch_attn<D, MT, NW, KT, KS, VS, false, DV>(p, grid, st);
 }
 
 }  // namespace
 
 // Prefill: 4 waves of 32 rows = 128 query rows per workgroup, 64-key tiles in
-// a 3-stage LDS ring (2 stages at head dim 128).
-fmha_status launch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st) {
+// a 3-stage LDS ring (2 stages at head dim 128).  Q/K head dim 192 with V/O
+// head dim 128: 2-stage K (24 KB tiles) and V (16 KB) rings, 80 KB.
+fmha_status launch_fwd(int D, int Dv, const AttnParams& p, dim3 grid, bool causal,
+                       hipStream_t st) {
+  if (D == 192 && Dv == 128) return launch_attn_c<192, 32, 4, 64, 2, 2, 128>(p, grid, causal, st);
+  if (Dv != D) return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dims D=%d, Dv=%d not built", D, Dv);
   switch (D) {
-    case 16: return launch_attn_cs<16, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
-    case 32: return launch_attn_cs<32, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
-    case 64: return launch_attn_cs<64, 32, 4, 64, 3, 3>(p, grid, causal, false, st);
-    case 128: return launch_attn_cs<128, 32, 4, 64, 2, 2>(p, grid, causal, false, st);
+    case 16: return launch_attn_c<16, 32, 4, 64, 3, 3>(p, grid, causal, st);
+    case 32: return launch_attn_c<32, 32, 4, 64, 3, 3>(p, grid, causal, st);
+    case 64: return launch_attn_c<64, 32, 4, 64, 3, 3>(p, grid, causal, st);
+    case 128: return launch_attn_c<128, 32, 4, 64, 2, 2>(p, grid, causal, st);
   }
   return fail(FMHA_ERR_HEAD_DIM, "fmha_fwd: head dim %d not built", D);
 }

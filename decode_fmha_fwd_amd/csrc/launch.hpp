@@ -66,7 +66,8 @@ inline bool decode_groups_built(int D, int Dv, bool kv_shared) {
 }
 
 // fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).
-fmha_status launch_fwd(int D, const AttnParams& p, dim3 grid, bool causal, hipStream_t st);
+fmha_status launch_fwd(int D, int Dv, const AttnParams& p, dim3 grid, bool causal,
+                       hipStream_t st);
 fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_out, int Sq,
                                 int Sk, int D, float scale, hipStream_t st);
 

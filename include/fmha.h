@@ -76,6 +76,20 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
                      void* stream);
 
 /*
+ * Attention forward with a V/O head dimension Dv different from the Q/K head
+ * dimension D (the workload list names the V head dimension apart from the
+ * Q/K one).  The built pair is D = 192, Dv = 128 (128 content dimensions plus
+ * 64 more key dimensions in Q and K).  Everything else is fmha_fwd:
+ *   q [B, Hq, Sq, D], k [B, Hkv, Sk, D], v [B, Hkv, Sk, Dv], o [B, Hq, Sq, Dv],
+ *   lse [B, Hq, Sq] or NULL.
+ *   (D, Dv): (192, 128), or D == Dv in {16, 32, 64, 128} (then exactly
+ *   fmha_fwd).  Anything else: FMHA_ERR_HEAD_DIM.
+ */
+fmha_status fmha_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale,
+                        int causal, void* stream);
+
+/*
  * Bytes of device workspace fmha_decode_splitkv needs for these sizes and this
  * number of splits (0 = the library's choice, see fmha_decode_default_splits).
  * Returns 0 when no workspace is needed (one split) or the sizes are invalid.

@@ -108,6 +108,26 @@ def test_dv_workspace_formula():
             F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 64, 16))
 
 
+def call_fwd_dv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=192,
+                Dv=128, scale=0.125, causal=0):
+    return F.load_library().fmha_fwd_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Dv=64), 3), (dict(D=128, Dv=192), 3), (dict(D=64, Dv=128), 3), (dict(Dv=192), 3),
+    (dict(D=576, Dv=512), 3), (dict(v=None), 1), (dict(Hq=3, Hkv=2), 4), (dict(o=FAKE + 4), 5),
+    (dict(Sq=5, Sk=4, causal=1), 2), (dict(scale=-1.0), 8),
+])
+def test_fwd_dv_validation(kw, status):
+    assert call_fwd_dv(**kw) == status
+    assert F.load_library().fmha_last_error()
+
+
+def test_fwd_192_needs_the_dv_entry_point():
+    assert call_fwd(D=192) == 3
+
+
 def call_paged(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, Hq=4, Hkv=1, Sq=1, sl=FAKE, bt=FAKE,
                mp=8, ps=64, npages=16, D=64, scale=0.125, causal=0, ns=4, ws=None, wsb=0):
     return F.load_library().fmha_decode_paged(q, k, v, o, lse, B, Hq, Hkv, Sq, sl, bt, mp, ps,

@@ -22,7 +22,8 @@ import torch
 class Workload:
     name: str
     kind: str            # "fwd" (prefill), "decode" (split-KV), "decode_nvfp4",
-                         # "decode_nvfp4_fused", "decode_paged", "decode_dv" (Dv != D)
+                         # "decode_nvfp4_fused", "decode_paged", "decode_dv" and
+                         # "fwd_dv" (Dv != D)
     B: int
     Hq: int
     Hkv: int
@@ -106,6 +107,8 @@ WORKLOADS = {
                  v_is_k=True,
                  note="the wide-head decode with V the same tensor as K (a shared latent): "
                       "each key row is streamed once"),
+        Workload("prefill_causal_d192_dv128", "fwd_dv", 4, 16, 16, 2048, 2048, 192, 128, 1.0, 6,
+                 True, note="causal prefill with Q/K head dim 192 and V/O head dim 128"),
         Workload("decode_mqa_d576_dv512_v_in_k", "decode_dv", 32, 64, 1, 1, 16384, 576, 512, 0.5,
                  5, False, v_is_k=True,
                  note="the wide-head decode with Q/K head dim 576 and V the first 512 columns "
