@@ -252,3 +252,26 @@ def test_split_groups_equal_one_workgroup_per_split(B, Hq, Hkv, Sq, Sk, D, causa
     rows = sample_rows(B * Hq * Sq, 64, seed=29)
     o_ref, lse_ref = oracle_rows(q, k, v, scale, causal, rows=rows)
     assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=f"B={B} D={D} grouped splits")
+
+
+# ---------------------------------------------------------------- long sequences
+
+def test_decode_one_million_keys():
+    """2^20 keys in 64 splits (256 MiB of K and V): key offsets past 2^26
+    elements, split lengths of 16384 keys; checked against the oracle."""
+    B, Hq, Hkv, Sq, Sk, D, ns = 1, 8, 1, 1, 1 << 20, 64, 64
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=41)
+    o, lse = run_decode(q, k, v, default_scale(D), False, ns)
+    o_ref, lse_ref = oracle_rows(q, k, v, default_scale(D), False)
+    assert_parity(o, lse, o_ref, lse_ref, what="1M keys")
+
+
+def test_prefill_causal_32k():
+    """One head, 32768 queries and keys, causal: 256 row blocks, the longest
+    streaming 512 key tiles; sampled rows against the oracle."""
+    B, H, S, D = 1, 1, 32768, 64
+    q, k, v = make_qkv(B, H, H, S, S, D, seed=43)
+    o, lse = run_fwd(q, k, v, default_scale(D), True)
+    rows = sample_rows(S, 48, seed=47)
+    o_ref, lse_ref = oracle_rows(q, k, v, default_scale(D), True, rows=rows)
+    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what="causal 32k")

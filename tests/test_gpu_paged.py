@@ -125,3 +125,15 @@ def test_paged_split_groups_with_empty_splits():
         o_ref, lse_ref = oracle_rows(q[b:b + 1], k[b:b + 1, :, :n].contiguous(),
                                      v[b:b + 1, :, :n].contiguous(), scale, False)
         assert_parity(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, what=f"batch {b} ({n} keys)")
+
+
+def test_paged_one_million_keys():
+    # 2^20 keys in 4096 shuffled 256-key pages: page ids and table slots in
+    # the thousands, key offsets past 2^26 elements
+    B, Hq, Hkv, D, P, S = 1, 4, 1, 64, 256, 1 << 20
+    q, k, v = make_qkv(B, Hq, Hkv, 1, S, D, seed=53)
+    kc, vc, table, num_pages = page_pool(k, v, [S], P, seed=59)
+    scale = default_scale(D)
+    o, lse = run_paged(q, kc, vc, [S], table, P, num_pages, scale, False, 32)
+    o_ref, lse_ref = oracle_rows(q, k, v, scale, False)
+    assert_parity(o, lse, o_ref, lse_ref, what="paged 1M keys")
