@@ -63,6 +63,9 @@ def parse():
                     help="HBM bytes per launch of --workload's kernels from rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counter CSVs of a bench run, scaled by the "
                          "same counters of a --copy-calibration run, then exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="AGENT_INFO_CSV then rocprofv3 counter_collection CSVs of one workload: "
+                         "per-kernel counter means and the derived utilisations, then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), as the "
                          "reference reading for HBM byte counters, then exit")
@@ -448,8 +451,69 @@ def cpu_nvfp4_sample(x, cols):
     return {"seconds": round(time.perf_counter() - t0, 5), "elements": int(xa.size)}
 
 
+def counter_summary(agent_csv, counter_csvs):
+    """Per attention/combine kernel: the mean of every SQ/GRBM counter over the
+    run's dispatches and rocprofv3's derived utilisations.  GRBM_GUI_ACTIVE
+    arrives summed over the XCDs, so the kernel's cycle count is that sum over
+    Num_Xcc; SQ_ACTIVE_INST_VALU, SQ_WAVE_CYCLES and SQ_WAIT_INST_ANY count
+    quad-cycles."""
+    gpu = [r for r in csv.DictReader(open(agent_csv, newline="")) if int(r.get("Simd_Count") or 0) > 0]
+    a = gpu[0]
+    nxcc, ncu, nsimd = int(a["Num_Xcc"]), int(a["Cu_Count"]), int(a["Simd_Count"])
+    per = {}
+    for path in counter_csvs:
+        with open(path, newline="") as fh:
+            for r in csv.DictReader(fh):
+                k = r["Kernel_Name"]
+                if "fmha::" not in k:
+                    continue
+                per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    print(f"agent: {ncu} CUs, {nsimd} SIMDs, {nxcc} XCDs")
+    for k, cs in per.items():
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        print(f"\n{k}")
+        for c in sorted(m):
+            print(f"  {c} = {m[c]:.0f}")
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / nxcc
+        if not cyc:
+            continue
+        out = {"kernel cycles (GRBM_GUI_ACTIVE / XCDs)": cyc}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out["MFMA busy, % of SIMD cycles"] = 100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * nsimd)
+            if m.get("SQ_INSTS_MFMA"):
+                out["MFMA busy cycles per MFMA instruction"] = (
+                    m["SQ_VALU_MFMA_BUSY_CYCLES"] / m["SQ_INSTS_MFMA"])
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            out["MFMA busy with a VALU issue, % of SIMD cycles"] = (
+                100 * m["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * nsimd))
+        if "SQ_ACTIVE_INST_VALU" in m:
+            out["VALU busy, %"] = 100 * m["SQ_ACTIVE_INST_VALU"] / ncu / cyc
+        if "SQ_WAVE_CYCLES" in m:
+            out["resident waves per CU (mean)"] = 4 * m["SQ_WAVE_CYCLES"] / cyc / ncu
+            if "SQ_WAIT_INST_ANY" in m:
+                out["wave time waiting to issue, %"] = (
+                    100 * m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"])
+        if "SQ_LDS_IDX_ACTIVE" in m:
+            out["LDS busy, %"] = 100 * m["SQ_LDS_IDX_ACTIVE"] / (cyc * ncu)
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            out["LDS bank-conflict cycles, %"] = 100 * m["SQ_LDS_BANK_CONFLICT"] / (cyc * ncu)
+        if m.get("SQ_INSTS_MFMA"):
+            mf = m["SQ_INSTS_MFMA"]
+            if "SQ_INSTS_VALU" in m:
+                out["VALU instructions per MFMA (SQ_INSTS_VALU / SQ_INSTS_MFMA)"] = (
+                    m["SQ_INSTS_VALU"] / mf)
+            if "SQ_INSTS_VALU_TRANS_F32" in m:
+                out["fp32 transcendentals per MFMA"] = m["SQ_INSTS_VALU_TRANS_F32"] / mf
+        for kk, vv in out.items():
+            print(f"  -> {kk}: {vv:.2f}")
+
+
 def main():
     args = parse()
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1:])
+        return
     if args.traffic_summary:
         from workloads import WORKLOADS
         traffic_summary(WORKLOADS[args.workload], *args.traffic_summary)

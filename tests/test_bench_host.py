@@ -69,3 +69,29 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, capsys):
 def test_workload_algorithmic_counts(name, flops, nbytes):
     w = WORKLOADS[name]
     assert w.flops() == flops and w.bytes() == nbytes
+
+
+def test_counter_summary_derived_metrics(tmp_path, capsys):
+    _write(tmp_path / "agent.csv", ["Agent_Type", "Num_Xcc", "Cu_Count", "Simd_Count"], [
+        {"Agent_Type": "CPU", "Num_Xcc": 1, "Cu_Count": 16, "Simd_Count": 0},
+        {"Agent_Type": "GPU", "Num_Xcc": 8, "Cu_Count": 256, "Simd_Count": 1024}])
+    k = "void fmha::attn_fwd_kernel<64>(p)"
+    rows = [{"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v} for c, v in [
+        ("GRBM_GUI_ACTIVE", 8 * 1000),            # 1000 cycles per XCD
+        ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250),  # 25 % of SIMD cycles
+        ("SQ_INSTS_MFMA", 1024 * 250 // 32),
+        ("SQ_ACTIVE_INST_VALU", 256 * 500),       # 50 %
+        ("SQ_WAVE_CYCLES", 256 * 1000 * 3 / 4),   # 3 waves per CU
+        ("SQ_WAIT_INST_ANY", 256 * 1000 * 3 / 8)]] + [
+        {"Kernel_Name": "void at::native::fill(x)", "Counter_Name": "GRBM_GUI_ACTIVE",
+         "Counter_Value": 5}]
+    _write(tmp_path / "c.csv", ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    bench.counter_summary(str(tmp_path / "agent.csv"), [str(tmp_path / "c.csv")])
+    out = capsys.readouterr().out
+    assert "kernel cycles (GRBM_GUI_ACTIVE / XCDs): 1000.00" in out
+    assert "MFMA busy, % of SIMD cycles: 25.00" in out
+    assert "MFMA busy cycles per MFMA instruction: 32.00" in out
+    assert "VALU busy, %: 50.00" in out
+    assert "resident waves per CU (mean): 3.00" in out
+    assert "wave time waiting to issue, %: 50.00" in out
+    assert "at::native" not in out
