@@ -28,8 +28,10 @@ fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 
     return launch_attn_cs<64, 16, 1, 32, 3, 3, false, false, 64, true>(p, grid, causal, split, st);
   if (D == 64 && c.nw == 4)
     return launch_attn_cs<64, 16, 4, 64, 3, 3, false, false, 64, true>(p, grid, causal, split, st);
+  // (head dim 128, one wave: a 3-deep K ring, 40 KB, four workgroups per CU --
+  // 2048 workgroups of the MHA decode then run in exactly two rounds)
   if (D == 128 && c.nw == 1)
-    return launch_attn_cs<128, 16, 1, 32, 2, 2, false, false, 128, true>(p, grid, causal, split, st);
+    return launch_attn_cs<128, 16, 1, 32, 3, 2, false, false, 128, true>(p, grid, causal, split, st);
   if (D == 128 && c.nw == 4)
     return launch_attn_cs<128, 16, 4, 64, 2, 2, false, false, 128, true>(p, grid, causal, split, st);
   if (D == 512) return launch_attn_cs<512, 16, 4, 32, 3, 2>(p, grid, causal, split, st);

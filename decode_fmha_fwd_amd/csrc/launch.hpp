@@ -54,7 +54,7 @@ struct DecodeCfg {
 // Must match the instantiations in fmha_decode.hip.
 inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
   if (D >= 512) return {4, 32, 1};
-  if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 5};
+  if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 4};
   return {4, 64, D == 64 ? 3 : 2};
 }
 
