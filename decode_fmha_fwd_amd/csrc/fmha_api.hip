@@ -180,6 +180,8 @@ fmha_status fmha_fwd_dv(const void* q, const void* k, const void* v, void* o, fl
                         int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale, int causal,
                         void* stream) {
   g_last_error[0] = 0;
+  if (k == v && Dv != D)  // the decode reads that as V inside the K rows
+    return fail(FMHA_ERR_ARG, "fmha_fwd_dv: V inside the K rows (v == k) is built for the decode only");
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, stream);
 }
 

@@ -83,7 +83,9 @@ fmha_status fmha_fwd(const void* q, const void* k, const void* v, void* o, float
  *   q [B, Hq, Sq, D], k [B, Hkv, Sk, D], v [B, Hkv, Sk, Dv], o [B, Hq, Sq, Dv],
  *   lse [B, Hq, Sq] or NULL.
  *   (D, Dv): (192, 128), or D == Dv in {16, 32, 64, 128} (then exactly
- *   fmha_fwd).  Anything else: FMHA_ERR_HEAD_DIM.
+ *   fmha_fwd).  Anything else: FMHA_ERR_HEAD_DIM.  v must be its own tensor:
+ *   the K buffer passed as V with Dv != D (the decode's "V inside the K
+ *   rows") is rejected with FMHA_ERR_ARG.
  */
 fmha_status fmha_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Hq, int Hkv, int Sq, int Sk, int D, int Dv, float scale,

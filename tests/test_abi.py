@@ -108,7 +108,7 @@ def test_dv_workspace_formula():
             F.fmha_decode_splitkv_workspace_size(64, 32, 8, 1, 8192, 64, 16))
 
 
-def call_fwd_dv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=192,
+def call_fwd_dv(q=FAKE, k=FAKE, v=2 * FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Sq=4, Sk=4, D=192,
                 Dv=128, scale=0.125, causal=0):
     return F.load_library().fmha_fwd_dv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal,
                                         None)
@@ -122,6 +122,11 @@ def call_fwd_dv(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Sq=4
 def test_fwd_dv_validation(kw, status):
     assert call_fwd_dv(**kw) == status
     assert F.load_library().fmha_last_error()
+
+
+def test_fwd_dv_rejects_v_inside_k():
+    assert call_fwd_dv(k=FAKE, v=FAKE) == 8
+    assert b"decode only" in F.load_library().fmha_last_error()
 
 
 def test_fwd_192_needs_the_dv_entry_point():
