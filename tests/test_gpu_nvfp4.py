@@ -153,6 +153,7 @@ FUSED_CASES = [
     (2, 8, 2, 1000, 64, 5),      # split: the combine kernel encodes
     (1, 64, 1, 700, 512, 3),
     (3, 16, 16, 257, 128, 2),
+    (64, 32, 8, 1000, 64, 8),    # 512 (batch, KV head) units: split groups, then the combine encodes
 ]
 
 
