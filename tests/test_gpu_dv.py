@@ -44,6 +44,8 @@ CASES = [
     (2, 32, 2, 1, 500, False, 1, False),
     (1, 32, 1, 2, 400, True, 2, False),
     (3, 8, 1, 1, 130, False, 2, False),    # 8 rows: a partly filled row block
+    (2, 64, 4, 1, 1500, False, 0, True),   # 4 KV heads of 16 rows, heuristic splits
+    (1, 16, 1, 3, 200, True, 2, False),    # three causal query rows (48 rows per KV head)
 ]
 
 
@@ -104,6 +106,8 @@ FWD_CASES = [
     (1, 2, 1, 77, 300, False),
     (1, 1, 1, 64, 1, False),        # one key
     (1, 2, 2, 600, 600, True),      # several 128-row blocks, the last ragged
+    (1, 2, 1, 300, 100, False),     # more queries than keys
+    (2, 6, 3, 129, 129, True),      # odd group size, one row past a 128-row block
 ]
 
 
