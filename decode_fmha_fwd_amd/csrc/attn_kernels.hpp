@@ -318,13 +318,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     const uint16_t* base;
     int t0, lim;
   };
-  // Page of key tile `it` in a paged cache (a scalar load of the block table;
-  // tiles past the range still get an in-bounds page: the table slot and the
-  // page id are clamped).
+  // Page of key tile `it` in a paged cache (tiles past the range still get an
+  // in-bounds page: the table slot and the page id are clamped).  The table
+  // is read through the constant address space (it is read-only while the
+  // kernel runs), so a uniform index makes a scalar load; a vector load would
+  // queue in the vector-memory counter behind the tile copies in flight, and
+  // the wait for its value would drain the whole copy ring every tile.
+  using ConstInt = const __attribute__((address_space(4))) int;
   auto page_of = [&](int it) {
     if constexpr (PAGED) {
       const int slot = min(max(kbeg + it * KT, 0) >> p.page_shift, p.bt_stride - 1);
-      return min(max(p.block_table[(long long)b * p.bt_stride + slot], 0), p.num_pages - 1);
+      ConstInt* table = (ConstInt*)p.block_table;
+      return min(max(table[(long long)b * p.bt_stride + slot], 0), p.num_pages - 1);
     } else {
       return 0;
     }

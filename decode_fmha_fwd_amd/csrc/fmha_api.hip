@@ -307,11 +307,10 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   // CU at least two workgroups and all fit the GPU's workgroup slots at once,
   // one workgroup streams all splits of its unit back to back (the same
   // partials, no short-lived workgroups).  Measured on the GQA decode (512
-  // units, 16 splits): 169 us against 178 us; with 1 unit per CU or fewer the
-  // split parallelism is needed, and partial groups measured slower.  A paged
-  // cache keeps one workgroup per split: its scattered pages need the many
-  // workgroups in flight (grouped: 262 us against 187 us).
-  if (!pg && decode_groups_built(D, Dv, kv_shared)) {
+  // units, 16 splits): 169 us against 178 us contiguous, 176 against 180 us
+  // from a shuffled page pool; with 1 unit per CU or fewer the split
+  // parallelism is needed, and partial groups measured slower.
+  if (decode_groups_built(D, Dv, kv_shared)) {
     const long long units = (long long)p.n_row_blocks * Hkv * B;
     if (units >= 2LL * num_cus() && units <= (long long)c.wgs_per_cu * num_cus())
       p.splits_per_wg = ns_eff;

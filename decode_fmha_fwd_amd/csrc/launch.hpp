@@ -60,7 +60,7 @@ inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
 
 // Decode configurations built with split groups (one workgroup streaming
 // several consecutive splits): head dims 64 and 128, two separate rings, a
-// contiguous cache.
+// contiguous or a paged cache.
 inline bool decode_groups_built(int D, int Dv, bool kv_shared) {
   return Dv == D && (D == 64 || D == 128) && !kv_shared;
 }

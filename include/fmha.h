@@ -214,8 +214,10 @@ fmha_status fmha_decode_splitkv_nvfp4(const void* q, const void* k, const void* 
  *   block_table: device int32 [B, max_pages_per_seq]; key j of batch b, KV
  *     head h, is row j % page_size of head h of page block_table[b][j / page_size].  Page ids are
  *     clamped to [0, num_pages), so a bad entry reads a wrong page, never
- *     outside the cache; only the first ceil(seqlens_k[b] / page_size)
- *     entries of a row are read.
+ *     outside the cache; only the pages of the first ceil(seqlens_k[b] /
+ *     page_size) entries of a row are read (later entries of the row may be
+ *     looked up ahead, never followed).  Neither array may change while the
+ *     call runs.
  *   page_size: a power of two, at least 64 (a key tile never straddles pages).
  *   causal: bottom-right aligned per batch (row i sees keys j <= i + len_b - Sq).
  *   Sk for the split choice and the workspace is max_pages_per_seq * page_size:

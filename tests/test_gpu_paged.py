@@ -127,6 +127,33 @@ def test_paged_split_groups_with_empty_splits():
         assert_parity(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref, what=f"batch {b} ({n} keys)")
 
 
+@pytest.mark.parametrize("Sq,D,causal,ns", [(1, 64, False, 8), (2, 64, True, 8),
+                                          (1, 128, False, 6)])
+def test_paged_split_groups_equal_one_workgroup_per_split(Sq, D, causal, ns):
+    # 64 batches x 8 KV heads (512 units: one workgroup streams all splits of
+    # a unit) with lengths from 0 to 1500 against single-batch calls (8 units:
+    # one workgroup per split), bit for bit, and the oracle
+    B, Hq, Hkv, P = 64, 32, 8, 64
+    lens = [int(x) for x in np.random.default_rng(D + Sq).integers(0, 1501, size=B)]
+    lens[0], lens[1], lens[2] = 1500, 0, 1
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, 1500, D, seed=61 + D + Sq)
+    kc, vc, table, num_pages = page_pool(k, v, lens, P, seed=67)
+    scale = default_scale(D)
+    o, lse = run_paged(q, kc, vc, lens, table, P, num_pages, scale, causal, ns)
+    for b in (0, 1, 2, B // 2, B - 1):
+        if causal and lens[b] < Sq:
+            continue  # causal attention needs at least Sq keys
+        o1, l1 = run_paged(q[b:b + 1], kc, vc, lens[b:b + 1], table[b:b + 1], P, num_pages,
+                           scale, causal, ns)
+        assert torch.equal(o[b].view(torch.int16), o1[0].view(torch.int16)), b
+        assert torch.equal(lse[b], l1[0]), b
+        if lens[b] > 0:
+            o_ref, lse_ref = oracle_rows(q[b:b + 1], k[b:b + 1, :, :lens[b]].contiguous(),
+                                         v[b:b + 1, :, :lens[b]].contiguous(), scale, causal)
+            assert_parity(o[b:b + 1], lse[b:b + 1], o_ref, lse_ref,
+                          what=f"batch {b} ({lens[b]} keys)")
+
+
 def test_paged_one_million_keys():
     # 2^20 keys in 4096 shuffled 256-key pages: page ids and table slots in
     # the thousands, key offsets past 2^26 elements
