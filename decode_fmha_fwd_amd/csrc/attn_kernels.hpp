@@ -191,6 +191,79 @@ __device__ inline void wait_vmcnt_at_most(int n) {
 // and bf16.  The final O / l and LSE are exact whichever maximum is used.
 constexpr float kRescaleSlack = 8.0f;
 
+// The combine of one wave's rows inside the attention kernel, for a split
+// group holding every split of its (batch, KV head): the arithmetic of
+// lse_combine_kernel row for row, so the output is bit-identical to the
+// split kernel followed by that kernel.  DV/4 lanes serve a row (4 outputs
+// each), 64/(DV/4) rows at a time; the combine kernel's 64 lanes, each with
+// the splits s = lane mod 64, are emulated by 64/(DV/4) "virtual lanes" per
+// lane, whose sums meet in the same tree order as its cross-lane butterfly.
+template <int DV>
+__device__ inline void combine_wave_rows(const float* __restrict__ o_part,
+                                         const float* __restrict__ lse_part, uint16_t* o,
+                                         float* lse, long long row0, int nrows, int nsplit,
+                                         int lane) {
+  static_assert(DV == 64 || DV == 128, "in-workgroup combine: head dims 64 and 128");
+  constexpr int VL = DV / 4;   // lanes per row
+  constexpr int G = 64 / VL;   // rows per pass, and virtual lanes per lane
+  const int li = lane % VL;
+  for (int r0 = 0; r0 < nrows; r0 += G) {
+    const int r = r0 + lane / VL;
+    const bool ok = r < nrows;
+    const long long row = row0 + (ok ? r : 0);  // idle lanes repeat row0 (in bounds)
+    const float* lp = lse_part + row * nsplit;
+    float m = -__builtin_inff();
+    for (int s = li; s < nsplit; s += VL) m = fmaxf(m, lp[s]);
+#pragma unroll
+    for (int msk = 1; msk < VL; msk <<= 1) m = fmaxf(m, xor_lane(m, msk));
+    if (m == -__builtin_inff()) {
+      if (ok) {
+        *(u32x2*)(o + row * DV + 4 * li) = u32x2{0u, 0u};
+        if (li == 0 && lse) lse[row] = -__builtin_inff();
+      }
+      continue;
+    }
+    // virtual lane k * VL + li holds the splits s = k * VL + li (mod 64)
+    float part[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      part[k] = 0.0f;
+      for (int s = k * VL + li; s < nsplit; s += 64) part[k] += __expf(lp[s] - m);
+#pragma unroll
+      for (int msk = 1; msk < VL; msk <<= 1) part[k] += xor_lane(part[k], msk);
+    }
+    // the butterfly's levels at lane masks VL .. 32
+#pragma unroll
+    for (int w = 1; w < G; w <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; k += 2 * w) part[k] = part[k] + part[k + w];
+    const float L = m + __logf(part[0]);
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float* op = o_part + row * nsplit * DV + 4 * li;
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {  // four splits' loads in flight, summed in order
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = *(const f32x4*)(op + (long long)(s + u) * DV);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __expf(lp[s + u] - L);
+        acc += w * x[u];
+      }
+    }
+    for (; s < nsplit; ++s) {
+      const float w = __expf(lp[s] - L);
+      acc += w * *(const f32x4*)(op + (long long)s * DV);
+    }
+    if (ok) {
+      *(u32x2*)(o + row * DV + 4 * li) =
+          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      if (li == 0 && lse) lse[row] = L;
+    }
+  }
+}
+
+
 // KST / VST: depth of the K and V rings (VST <= KST <= VST + 1).  V is read
 // after K within a tile, so with one K stage more than V stages the extra
 // look-ahead costs a K tile of LDS rather than a K and a V tile.
@@ -696,6 +769,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
       for (int j = s_done; j < nspl; ++j) {
         write_partial(split0 + j);
         reset_state();
+      }
+      if constexpr (DV == 64 || DV == 128) {
+        if (p.combine_in_wg) {  // every split of the unit is here: combine in place
+          __syncthreads();      // the partial stores of every lane are visible
+          const int nr = min(MT, p.rows_per_kv - r_wave0);
+          if (nr > 0)
+            combine_wave_rows<DV>(p.o_part, p.lse_part, p.o, p.lse, row_base + r_wave0, nr,
+                                  p.nsplit, lane);
+        }
       }
     } else {
       write_partial(split0);

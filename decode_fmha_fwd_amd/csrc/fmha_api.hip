@@ -315,10 +315,14 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
     if (units >= 2LL * num_cus() && units <= (long long)c.wgs_per_cu * num_cus())
       p.splits_per_wg = ns_eff;
   }
+  // A workgroup holding every split of its unit combines them itself (the
+  // combine kernel's arithmetic; the amax fold and the NVFP4 output stay with
+  // that kernel): one launch fewer.
+  p.combine_in_wg = (p.splits_per_wg == ns_eff && !o_amax && !fp4_codes) ? 1 : 0;
   const int nsg = (ns_eff + p.splits_per_wg - 1) / p.splits_per_wg;
   dim3 grid((unsigned)p.n_row_blocks * nsg * Hkv * B);
   s = attention(grid, true);
-  if (s != FMHA_OK) return s;
+  if (s != FMHA_OK || p.combine_in_wg) return s;
   return launch_combine(Dv, p.o_part, p.lse_part, (uint16_t*)o, lse, o_amax, fp4_codes,
                         fp4_scales, fp4_gscale, (long long)rows, ns_eff, st);
 }

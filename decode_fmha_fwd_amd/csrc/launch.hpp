@@ -30,6 +30,7 @@ struct AttnParams {
   int nsplit;           // key ranges per (batch, KV head)
   int split_len;        // keys per range, a multiple of KT
   int splits_per_wg;    // consecutive splits one workgroup takes (split groups), >= 1
+  int combine_in_wg;    // split groups holding every split: the kernel combines them
   float scale_log2;     // scale * log2(e)
   // Paged KV cache (decode only).  K and V are [num_pages][Hkv][page_size][D];
   // key j of batch b sits in page block_table[b * bt_stride + j / page_size].
