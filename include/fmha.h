@@ -107,8 +107,10 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  * all ranges of its (batch, KV head) back to back when those units alone fill
  * the GPU, and writes an fp32 partial output and its log-sum-exp per range to
  * the workspace; a second kernel combines them:  LSE = m + log sum_s exp(lse_s - m),  m = max_s lse_s,
- * O = sum_s exp(lse_s - LSE) * O_s.   With one split the first kernel writes
- * O and LSE directly and no workspace is used.
+ * O = sum_s exp(lse_s - LSE) * O_s  (a workgroup that holds all ranges of its
+ * (batch, KV head) combines them itself, with the same arithmetic, unless
+ * o_amax is given).  With one split the first kernel writes O and LSE
+ * directly and no workspace is used.
  *   D in {64, 128, 512}; the Sq*Hq/Hkv rows of a KV head are taken in
  *   blocks of 16 or 64 (one workgroup each).
  *   num_splits: 0 = heuristic, otherwise 1..1024.
