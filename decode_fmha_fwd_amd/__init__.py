@@ -45,7 +45,7 @@ SIGNATURES = {
                                     _P, _SZ, _P]),
     "nvfp4_quantize_workspace_size": (_SZ, [_LL, _I]),
     "nvfp4_quantize": (_I, [_P, _LL, _I, _P, _P, _P, _P, _P, _SZ, _P]),
-    "fmha_debug_qk_scores": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
+    "fmha_debug_qk_scores": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fmha_status_string": (ctypes.c_char_p, [_I]),
     "fmha_last_error": (ctypes.c_char_p, []),
 }
@@ -186,11 +186,12 @@ def nvfp4_quantize(x, rows, cols, codes, scales, global_scale, amax_in=None, wor
                               _ptr(amax_in), _ptr(workspace), int(workspace_bytes), st))
 
 
-def fmha_debug_qk_scores(q, k, s_out, Sq, Sk, D, scale, stream=None):
+def fmha_debug_qk_scores(q, k, v, s_out, B, Hq, Hkv, Sq, Sk, D, Dv, scale, decode, stream=None):
     lib = load_library()
     st = stream if stream is not None else _stream(q.device)
     _check("fmha_debug_qk_scores",
-           lib.fmha_debug_qk_scores(_ptr(q), _ptr(k), _ptr(s_out), Sq, Sk, D, float(scale), st))
+           lib.fmha_debug_qk_scores(_ptr(q), _ptr(k), _ptr(v), _ptr(s_out), B, Hq, Hkv, Sq, Sk, D,
+                                    Dv, float(scale), int(decode), st))
 
 
 # ---------------------------------------------------------------- conveniences

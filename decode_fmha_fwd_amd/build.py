@@ -41,6 +41,12 @@ PER_FILE = {
     # prefill keeps MFMA accumulators in ordinary VGPRs (no AGPR round trips
     # around the softmax); decode at head dim 512 needs the AGPR file for O
     "fmha_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # test-only score stores: the flags of the prefill and decode units
+    # (accumulators in VGPRs would change the decode's register budget, so
+    # the debug unit keeps the decode's default; the prefill's QK block
+    # compiles to the same instructions either way)
+    "fmha_debug.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt",
+                       "-fno-gpu-flush-denormals-to-zero"],
     # the decode epilogues can encode NVFP4: the same fp32 semantics as nvfp4.hip
     "fmha_decode.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt",
                         "-fno-gpu-flush-denormals-to-zero"],
@@ -50,8 +56,8 @@ PER_FILE = {
                   "-fno-gpu-flush-denormals-to-zero"],
 }
 SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip",
-           "nvfp4.hip"]
-ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip"}
+           "fmha_debug.hip", "nvfp4.hip"]
+ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip", "fmha_debug.hip"}
 
 
 def hipcc() -> str:

@@ -105,36 +105,6 @@ __device__ inline void load_q_frags(const uint16_t* qrow, int kg,
   }
 }
 
-// The QK product of one KV tile: S^T[key][query] for KBLK blocks of MT keys,
-// K read from the swizzled LDS tile as the A operand (lane holds
-// K[kb*MT + lane % MT][s*kK + 8*(lane / MT) + 0..7]).  The raw dot products
-// are returned; the softmax scale is applied by the caller.
-template <int D, int MT, int KBLK>
-__device__ inline void qk_scores(const uint16_t* ks,
-                                 const bf16x8 (&qf)[(D + Mfma<MT>::kK - 1) / Mfma<MT>::kK],
-                                 int lane, typename Mfma<MT>::Acc (&sacc)[KBLK]) {
-  using M = Mfma<MT>;
-  constexpr int KSTEPS = (D + M::kK - 1) / M::kK;
-  const int kg = lane / MT;
-  u32x4 kf[KBLK][KSTEPS];
-#pragma unroll
-  for (int kb = 0; kb < KBLK; ++kb) {
-    const int krow = kb * MT + lane % MT;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int col = s * M::kK + 8 * kg;
-      kf[kb][s] = lds_read_b128((const FMHA_LDS void*)&ks[tile_off<D>(krow, col < D ? col : 0)]);
-    }
-  }
-#pragma unroll
-  for (int kb = 0; kb < KBLK; ++kb) sacc[kb] = typename M::Acc{};
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-    for (int kb = 0; kb < KBLK; ++kb)
-      sacc[kb] = M::run(__builtin_bit_cast(bf16x8, kf[kb][s]), qf[s], sacc[kb]);
-}
-
 // Copies one K or V tile (KT rows of W bf16 taken at column col0 of rows that
 // are `stride` elements apart; rows clamped to the last key for a ragged tail)
 // into a swizzled LDS tile with asynchronous global->LDS copies.  Each wave
@@ -286,8 +256,14 @@ __device__ inline void combine_wave_rows(const float* __restrict__ o_part,
 // runs through all of them; at every split boundary the softmax state is
 // written out as that split's partial and reset, which is the arithmetic of
 // one workgroup per split, without a short-lived workgroup per split.
+//
+// DBG_S (test builds only): after the QK block of every tile, the raw score
+// tile times p.s_dbg_scale is stored to p.s_dbg [rows][Sk] (before masking and
+// softmax), and the kernel writes no output.  Everything else -- copies, ring,
+// LDS reads, MFMA chains -- is the code of the kernel without the flag.
 template <int D, int MT, int NW, int KT, int KST, int VST, bool CAUSAL, bool SPLIT,
-          bool KVS = false, bool PAGED = false, int DV = D, bool GROUP = false>
+          bool KVS = false, bool PAGED = false, int DV = D, bool GROUP = false,
+          bool DBG_S = false>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   using M = Mfma<MT>;
   using Acc = typename M::Acc;
@@ -613,6 +589,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb) sacc[kb] += sodd[kb];
     }
+    if constexpr (DBG_S) {
+      if (row_ok) {
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int r = 0; r < M::kRegs; ++r) {
+            const int key = t0 + kb * MT + acc_row<MT>(lane, r);
+            if (key < kend)
+              p.s_dbg[(row_base + my_r) * (long long)p.Sk + key] = sacc[kb][r] * p.s_dbg_scale;
+          }
+      }
+    }
 
     // ---- mask the ragged end and the causal diagonal ----
     const bool need_mask = (t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last);
@@ -761,6 +749,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     });
   }
 
+  if constexpr (DBG_S) return;
+
   // ---- epilogue: O / l, log-sum-exp ----
   if constexpr (SPLIT) {
     if constexpr (GROUP) {
@@ -843,38 +833,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         }
       }
     }
-  }
-}
-
-// Test hook: raw scores S = scale * Q K^T for Sq, Sk <= 128 of the first
-// (batch, head), through the same load_q_frags / qk_scores path as the
-// attention kernel (4 waves x 32 query rows, one 128-key tile).
-template <int D>
-__global__ __launch_bounds__(256) void qk_scores_debug_kernel(const uint16_t* q, const uint16_t* k,
-                                                              float* s_out, int Sq, int Sk,
-                                                              float scale) {
-  constexpr int MT = 32, KT = 128, KBLK = KT / MT, CPR = D / 8;
-  using Acc = typename Mfma<MT>::Acc;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[KT * D];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int idx = tid; idx < KT * CPR; idx += 256) {
-    const int row = idx / CPR, ch = idx % CPR;
-    const int key = min(row, Sk - 1);
-    lds_write_b128((FMHA_LDS void*)&ks[row * D + ((ch ^ swz<CPR>(row)) << 3)],
-                   *(const u32x4*)(k + (long long)key * D + ch * 8));
-  }
-  __syncthreads();
-  const int qrow = wave * MT + lane % MT;
-  bf16x8 qf[(D + 15) / 16];
-  load_q_frags<D, MT>(q + (long long)min(qrow, Sq - 1) * D, lane / MT, qf);
-  Acc sacc[KBLK];
-  qk_scores<D, MT, KBLK>(ks, qf, lane, sacc);
-  if (qrow < Sq) {
-    for (int kb = 0; kb < KBLK; ++kb)
-      for (int r = 0; r < Mfma<MT>::kRegs; ++r) {
-        const int key = kb * MT + acc_row<MT>(lane, r);
-        if (key < Sk) s_out[(long long)qrow * Sk + key] = sacc[kb][r] * scale;
-      }
   }
 }
 

@@ -80,6 +80,10 @@ int num_cus() {
   return cus;
 }
 
+// Clears the amax accumulator of a decode call (a kernel on the call's stream,
+// so the whole call can be captured in a graph).
+__global__ void clear_f32_kernel(float* p) { *p = 0.0f; }
+
 // Keys per split: equal ranges rounded up to the KV tile.
 int split_len_for(int Sk, int nsplit, int kt) {
   int len = (Sk + nsplit - 1) / nsplit;
@@ -281,6 +285,11 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   }
   const hipStream_t st = (hipStream_t)stream;
   if (!grid_fits(p.n_row_blocks, ns_eff, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
+  if (o_amax) {
+    hipLaunchKernelGGL(clear_f32_kernel, dim3(1), dim3(1), 0, st, o_amax);
+    s = check_launch("amax clear launch");
+    if (s != FMHA_OK) return s;
+  }
 
   // V aliasing K (the same buffer): at head dim 512, or with V the first Dv
   // columns of the K rows, each key row is then streamed from HBM once and
@@ -396,16 +405,43 @@ fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_
                      nullptr, nullptr, &pg, stream);
 }
 
-fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,
-                                 int D, float scale, void* stream) {
+fmha_status fmha_debug_qk_scores(const void* q, const void* k, const void* v, float* s_out,
+                                 int B, int Hq, int Hkv, int Sq, int Sk, int D, int Dv,
+                                 float scale, int decode, void* stream) {
   g_last_error[0] = 0;
-  if (!q || !k || !s_out) return fail(FMHA_ERR_NULL, "q, k and s_out must be non-null");
-  if (Sq < 1 || Sk < 1 || Sq > 128 || Sk > 128)
-    return fail(FMHA_ERR_SHAPE, "debug scores need 1 <= Sq, Sk <= 128");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(s_out))
-    return fail(FMHA_ERR_ALIGN, "q, k and s_out must be 16-byte aligned");
-  return launch_debug_scores((const uint16_t*)q, (const uint16_t*)k, s_out, Sq, Sk, D, scale,
-                             (hipStream_t)stream);
+  if (!s_out) return fail(FMHA_ERR_NULL, "s_out must be non-null");
+  fmha_status s = check_common(q, k, v, s_out, B, Hq, Hkv, Sq, Sk, scale, 0);
+  if (s != FMHA_OK) return s;
+  if (decode != 0 && decode != 1) return fail(FMHA_ERR_ARG, "decode must be 0 or 1");
+  if (decode ? !decode_dims_ok(D, Dv) : !fwd_dims_ok(D, Dv))
+    return fail(FMHA_ERR_HEAD_DIM, "debug scores: head dims D=%d, Dv=%d not built", D, Dv);
+  if (!decode && k == v && Dv != D)
+    return fail(FMHA_ERR_ARG, "debug scores: V inside the K rows is built for the decode only");
+  if ((long long)B * Hq * Sq * Sk >= (1LL << 31))
+    return fail(FMHA_ERR_SHAPE, "debug scores: s_out larger than 2^31 elements");
+  const int rows_per_kv = (Hq / Hkv) * Sq;
+  const DecodeCfg c = decode ? decode_cfg(D, rows_per_kv) : DecodeCfg{4, 64, 3};
+  const int rows_wg = decode ? 16 * c.nw : 128;
+  AttnParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.B = B;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.rows_per_kv = rows_per_kv;
+  p.n_row_blocks = (rows_per_kv + rows_wg - 1) / rows_wg;
+  p.nsplit = 1;
+  p.split_len = (Sk + c.kt - 1) / c.kt * c.kt;
+  p.splits_per_wg = 1;
+  p.scale_log2 = scale * kLog2e;
+  p.s_dbg = s_out;
+  p.s_dbg_scale = scale;
+  if (!grid_fits(p.n_row_blocks, 1, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
+  const bool kv_shared = decode && (k == v) && (D == 512 || Dv < D);
+  dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
+  return launch_debug_scores(D, Dv, c, p, grid, decode != 0, kv_shared, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -39,6 +39,9 @@ struct AttnParams {
   int bt_stride;
   int page_shift;          // log2(page_size); page_size is a power of two >= 64
   int num_pages;
+  // Test builds (DBG_S) only: raw score tiles times s_dbg_scale, [rows][Sk].
+  float* s_dbg;
+  float s_dbg_scale;
 };
 
 // Tile configuration of the decode kernel for a head dim and a row count.
@@ -52,7 +55,7 @@ struct DecodeCfg {
 // small workgroups keep enough loads in flight per CU); four waves otherwise.
 // Head dim 512 (and 576 with V/O at 512): four waves sharing 32-key tiles in
 // rings that take most of the CU's 160 KB of LDS.
-// Must match the instantiations in fmha_decode.hip.
+// Must match the configurations of with_decode_cfg below.
 inline DecodeCfg decode_cfg(int D, int rows_per_kv) {
   if (D >= 512) return {4, 32, 1};
   if (rows_per_kv <= 16) return {1, 32, D == 64 ? 6 : 4};
@@ -66,11 +69,62 @@ inline bool decode_groups_built(int D, int Dv, bool kv_shared) {
   return Dv == D && (D == 64 || D == 128) && !kv_shared;
 }
 
+// Compile-time tile configuration of one attention kernel instantiation.
+template <int D_, int MT_, int NW_, int KT_, int KS_, int VS_, bool KVS_ = false, int DV_ = D_,
+          bool GROUPS_ = false>
+struct TileCfg {
+  static constexpr int D = D_, MT = MT_, NW = NW_, KT = KT_, KS = KS_, VS = VS_, DV = DV_;
+  static constexpr bool KVS = KVS_, GROUPS = GROUPS_;
+};
+
+// The prefill kernel configurations (4 waves x 32 query rows, 64-key tiles):
+// calls f(TileCfg<...>{}) for the (D, Dv) pair and returns its status, or
+// FMHA_ERR_HEAD_DIM.  2-stage LDS rings at head dims 64 and 128 (3 stages at
+// 16 and 32; at 64 the 2-stage rings, 32 KB, measured 1-2 % faster than 3
+// stages, 48 KB, and 4 stages 5-8 % slower).  Q/K head dim 192 with V/O head
+// dim 128: 2-stage K (24 KB tiles) and V (16 KB) rings, 80 KB.
+template <class F>
+fmha_status with_fwd_cfg(int D, int Dv, F&& f) {
+  if (D == 192 && Dv == 128) return f(TileCfg<192, 32, 4, 64, 2, 2, false, 128>{});
+  if (Dv == D) {
+    switch (D) {
+      case 16: return f(TileCfg<16, 32, 4, 64, 3, 3>{});
+      case 32: return f(TileCfg<32, 32, 4, 64, 3, 3>{});
+      case 64: return f(TileCfg<64, 32, 4, 64, 2, 2>{});
+      case 128: return f(TileCfg<128, 32, 4, 64, 2, 2>{});
+    }
+  }
+  return FMHA_ERR_HEAD_DIM;
+}
+
+// The contiguous-cache decode kernel configurations (16-row waves), chosen by
+// head dims, the row-count configuration c and whether V is the first Dv
+// columns of the K rows (kv_shared); FMHA_ERR_HEAD_DIM if none is built.
+//   576 / 512, V inside the K rows: one 4-deep ring of 32-key K tiles (144 KB);
+//   576 / 512, separate V: 2-deep K and V rings (136 KB).
+//   512, V aliasing K: one 5-deep ring of 32-key tiles (160 KB).
+//   64 and 128 also come with split groups (GROUPS; see decode_groups_built);
+//   128 with one wave: a 3-deep K ring, 40 KB, four workgroups per CU (2048
+//   workgroups of the MHA decode then run in exactly two rounds).
+template <class F>
+fmha_status with_decode_cfg(int D, int Dv, DecodeCfg c, bool kv_shared, F&& f) {
+  if (D == 576 && Dv == 512) {
+    if (kv_shared) return f(TileCfg<576, 16, 4, 32, 4, 4, true, 512>{});
+    return f(TileCfg<576, 16, 4, 32, 2, 2, false, 512>{});
+  }
+  if (Dv != D) return FMHA_ERR_HEAD_DIM;
+  if (D == 512 && kv_shared) return f(TileCfg<512, 16, 4, 32, 5, 5, true>{});
+  if (D == 64 && c.nw == 1) return f(TileCfg<64, 16, 1, 32, 3, 3, false, 64, true>{});
+  if (D == 64 && c.nw == 4) return f(TileCfg<64, 16, 4, 64, 3, 3, false, 64, true>{});
+  if (D == 128 && c.nw == 1) return f(TileCfg<128, 16, 1, 32, 3, 2, false, 128, true>{});
+  if (D == 128 && c.nw == 4) return f(TileCfg<128, 16, 4, 64, 2, 2, false, 128, true>{});
+  if (D == 512) return f(TileCfg<512, 16, 4, 32, 3, 2>{});
+  return FMHA_ERR_HEAD_DIM;
+}
+
 // fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).
 fmha_status launch_fwd(int D, int Dv, const AttnParams& p, dim3 grid, bool causal,
                        hipStream_t st);
-fmha_status launch_debug_scores(const uint16_t* q, const uint16_t* k, float* s_out, int Sq,
-                                int Sk, int D, float scale, hipStream_t st);
 
 // fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
 // D: head dim of Q/K, Dv: of V/O; kv_shared: V is the first Dv columns of the
@@ -80,6 +134,10 @@ fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 
 // The same decode reading K/V from a paged cache (p.seqlens, p.block_table set).
 fmha_status launch_decode_paged(int D, DecodeCfg c, const AttnParams& p, dim3 grid, bool causal,
                                 bool split, hipStream_t st);
+// fmha_debug.hip: the same prefill (decode = false) or one-split decode
+// kernels built with DBG_S (p.s_dbg, p.s_dbg_scale set), non-causal.
+fmha_status launch_debug_scores(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 grid,
+                                bool decode, bool kv_shared, hipStream_t st);
 fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,
                            float* lse, float* o_amax, uint8_t* fp4_codes, uint8_t* fp4_scales,
                            const float* fp4_gscale, long long nrows, int nsplit,

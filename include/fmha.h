@@ -116,9 +116,10 @@ size_t fmha_decode_splitkv_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  *   num_splits: 0 = heuristic, otherwise 1..1024.
  *   workspace / workspace_bytes: device buffer of at least
  *     fmha_decode_splitkv_workspace_size(...) bytes (may be NULL when that is 0).
- *   o_amax: NULL, or a device fp32 that the call raises to max(*o_amax, max|O|)
- *     over the bf16 O it writes (the caller initialises it, e.g. to 0); this
- *     folds the NVFP4 quantiser's tensor-wide amax into the decode.
+ *   o_amax: NULL, or a device fp32 that receives max|O| over the bf16 O the
+ *     call writes (the call clears it first, with a kernel on `stream`); this
+ *     folds the NVFP4 quantiser's tensor-wide amax into the decode, so
+ *     nvfp4_quantize(..., amax_in = o_amax, ...) needs no amax pass.
  */
 fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
@@ -238,14 +239,28 @@ fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Test hook: the raw score tile S = scale * Q K^T of the first (batch, head),
- * for Sq, Sk <= 128 and D in {16, 32, 64, 128}, computed by the same device
- * routine the attention kernels use for their QK product; s_out is fp32
- * [Sq, Sk].  Lets a test check the product against the exact scalar dot
- * product on integer-valued inputs (a 4x-class fault cannot hide).
+ * Test hook: the raw scores S = scale * Q K^T of every (query row, key) pair,
+ * computed by the QK block of the attention kernel itself -- the global->LDS
+ * copy ring, the inline-asm LDS reads of K and the MFMA accumulation chains
+ * of the production kernel, built with a flag that stores each score tile as
+ * it leaves that block (before masking and softmax) and skips the outputs.
+ * The page "CURRENT ISSUE: UMMA QK GEMM -- 4x Scaling Bug" (sections "The 4x
+ * Bug" and "How to fix") is why: its MMA result differed from the scalar dot
+ * product by a factor of 4; on integer-valued inputs every partial sum here is
+ * exact, so S must equal scale * <q, k> bit for bit.
+ *   decode = 0: the prefill kernel fmha_fwd / fmha_fwd_dv would launch for
+ *     (D, Dv) (32-row waves, 32x32x16 MFMAs); decode = 1: the one-split
+ *     kernel fmha_decode_splitkv / _dv would launch (16-row waves, 16x16x32
+ *     MFMAs), with v == k selecting the shared-ring form where that exists.
+ *   q, k, v: as for those calls; non-causal.
+ *   s_out: fp32 [B * Hq * Sq, Sk] (row = (b * Hq + h) * Sq + i), every entry
+ *     written; B * Hq * Sq * Sk < 2^31.
+ * Errors: the argument checks of the matching call, FMHA_ERR_HEAD_DIM for a
+ * (D, Dv) pair that path is not built for.
  */
-fmha_status fmha_debug_qk_scores(const void* q, const void* k, float* s_out, int Sq, int Sk,
-                                 int D, float scale, void* stream);
+fmha_status fmha_debug_qk_scores(const void* q, const void* k, const void* v, float* s_out,
+                                 int B, int Hq, int Hkv, int Sq, int Sk, int D, int Dv,
+                                 float scale, int decode, void* stream);
 
 const char* fmha_status_string(fmha_status s);
 

@@ -186,6 +186,21 @@ def test_nvfp4_validation():
 
 def test_debug_scores_validation():
     lib = F.load_library()
-    assert lib.fmha_debug_qk_scores(FAKE, FAKE, FAKE, 129, 4, 64, 1.0, None) == 2
-    assert lib.fmha_debug_qk_scores(FAKE, FAKE, FAKE, 4, 4, 512, 1.0, None) == 3
-    assert lib.fmha_debug_qk_scores(None, FAKE, FAKE, 4, 4, 64, 1.0, None) == 1
+    d = lib.fmha_debug_qk_scores
+
+    def call(q=FAKE, k=FAKE, v=FAKE, s=FAKE, B=1, Hq=4, Hkv=1, Sq=4, Sk=64, D=64, Dv=64,
+             scale=0.125, decode=0):
+        return d(q, k, v, s, B, Hq, Hkv, Sq, Sk, D, Dv, scale, decode, None)
+
+    assert call(s=None) == 1
+    assert call(q=None) == 1
+    assert call(Sk=0) == 2
+    assert call(B=1 << 12, Hq=1 << 12, Sk=1 << 8) == 2   # s_out past 2^31 elements
+    assert call(D=512, Dv=512) == 3                       # no 512 prefill
+    assert call(D=16, Dv=16, decode=1) == 3               # no 16 decode
+    assert call(D=576, Dv=512) == 3                       # 576/512 is decode only
+    assert call(D=192, Dv=128, decode=1) == 3             # 192/128 is prefill only
+    assert call(Hq=3, Hkv=2) == 4
+    assert call(s=FAKE + 4) == 5
+    assert call(decode=2) == 8
+    assert call(D=192, Dv=128, v=FAKE) == 8               # V inside K: decode only

@@ -15,15 +15,28 @@ def _write(path, fields, rows):
         w.writerows(rows)
 
 
-def test_trace_summary_takes_the_last_steps_of_each_workload(tmp_path, capsys):
+def test_trace_summary_takes_the_flushed_and_back_to_back_dispatches(tmp_path, capsys):
     # two workloads separated by a 2 s gap; the first runs 5 untimed launches
-    # of 100 us, then 3 timed ones of 40 us
+    # of 100 us, then 3 flushed ones of 50 us (each after a flush fill kernel),
+    # then 3 back-to-back ones of 40 us
     rows, t = [], 0
-    for dur in [100] * 5 + [40] * 3:
-        rows.append({"Kernel_Name": "attnA", "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+    for dur in [100] * 5:
+        rows.append({"Kernel_Name": "attn_fwd_kernelA", "Start_Timestamp": t,
+                     "End_Timestamp": t + dur * 1000})
+        t += 200_000
+    for dur in [50, 52, 48]:
+        rows.append({"Kernel_Name": "void at::native::fill", "Start_Timestamp": t,
+                     "End_Timestamp": t + 90_000})
+        t += 100_000
+        rows.append({"Kernel_Name": "attn_fwd_kernelA", "Start_Timestamp": t,
+                     "End_Timestamp": t + dur * 1000})
+        t += 200_000
+    for dur in [40] * 3:
+        rows.append({"Kernel_Name": "attn_fwd_kernelA", "Start_Timestamp": t,
+                     "End_Timestamp": t + dur * 1000})
         t += 200_000
     t += 2_000_000_000
-    for dur in [7, 7, 9, 9, 9]:
+    for dur in [7, 7, 9, 9, 9, 9, 9]:
         for k in ("attnB", "combine"):
             rows.append({"Kernel_Name": k, "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
             t += 50_000
@@ -32,9 +45,13 @@ def test_trace_summary_takes_the_last_steps_of_each_workload(tmp_path, capsys):
     bench.trace_summary(str(p), 3, ["first", "second"])
     out = capsys.readouterr().out.splitlines()
     body = [ln for ln in out if ln.startswith("| first") or ln.startswith("| second")]
-    assert len(body) == 3
-    assert "`attnA` | 3 | 40.00 | 40.00 | 40.00" in body[0]
-    assert "`attnB` | 3 | 9.00 |" in body[1] and "`combine` | 3 | 9.00 |" in body[2]
+    assert len(body) == 6  # the flush fill kernel is left out
+    assert "`attn_fwd_kernelA` | flushed | 3 | 50.00 | 50.00 | 48.00 | 52.00" in body[0]
+    assert "`attn_fwd_kernelA` | back-to-back | 3 | 40.00 | 40.00 | 40.00 | 40.00" in body[1]
+    assert "`attnB` | flushed | 3 | 8.33 |" in body[2] and "`attnB` | back-to-back | 3 | 9.00 |" in body[3]
+    assert "`combine` | back-to-back | 3 | 9.00 |" in body[5]
+    machine = [ln for ln in out if ln.startswith("trace_kernel_us_back_to_back")]
+    assert len(machine) == 1 and machine[0].split()[1:3] == ["first", "40.000"]
 
 
 def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, capsys):

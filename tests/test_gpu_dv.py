@@ -8,7 +8,7 @@ import torch
 
 import decode_fmha_fwd_amd as F
 from gpu_helpers import assert_parity, oracle_rows, poison_like, require_gpu
-from workloads import WORKLOADS, default_scale, make_qkv, make_workload_inputs, sample_rows, v_of
+from workloads import WORKLOADS, default_scale, make_qkv, make_workload_inputs, v_of
 
 pytestmark = pytest.mark.gpu
 
@@ -75,15 +75,14 @@ def test_decode_dv_uses_only_the_first_dv_columns():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_decode_dv_workload_sampled():
+def test_decode_dv_workload():
+    """The full-size 576/512 decode with V inside the K rows, every row."""
     w = WORKLOADS["decode_mqa_d576_dv512_v_in_k"]
     q, k, v = make_workload_inputs(w)
     assert v is k
     o, lse = run_decode_dv(q, k, k, w.Dv, w.scale, w.causal, w.num_splits)
-    rows = sample_rows(w.B * w.Hq * w.Sq, 64, seed=17)
-    o_ref, lse_ref = oracle_rows(q, k, v_of(k, w.Dv), w.scale, w.causal, rows=rows)
-    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=w.name)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = oracle_rows(q, k, v_of(k, w.Dv), w.scale, w.causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=w.name)
 
 
 def test_decode_dv_equal_dims_match_the_plain_decode():
@@ -133,11 +132,10 @@ def test_fwd_dv_small_shapes(case):
     assert_parity(o, lse, o_ref, lse_ref, what=str(case))
 
 
-def test_fwd_dv_workload_sampled():
+def test_fwd_dv_workload():
+    """The full-size 192/128 causal prefill, every row."""
     w = WORKLOADS["prefill_causal_d192_dv128"]
     q, k, v = make_workload_inputs(w)
     o, lse = run_fwd_dv(q, k, v, w.scale, w.causal)
-    rows = sample_rows(w.B * w.Hq * w.Sq, 256, seed=31)
-    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal, rows=rows)
-    assert_parity(o, lse, o_ref, lse_ref, rows=rows, what=w.name)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=w.name)

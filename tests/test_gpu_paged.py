@@ -105,6 +105,8 @@ def test_paged_gqa_decode_workload_equals_contiguous():
     del kc, vc
     o2, l2 = run_contiguous(q, k, v, w.scale, w.causal, w.num_splits)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    o_ref, lse_ref = oracle_rows(q, k, v, w.scale, w.causal)  # and every row against the oracle
+    assert_parity(o1, l1, o_ref, lse_ref, what="paged " + w.name)
 
 
 def test_paged_split_groups_with_empty_splits():

@@ -2,7 +2,7 @@
 
 Every entry point launches on the stream it is given and on nothing else, so
 a graph captured on torch's capture stream holds the whole call (split
-kernels, combine, amax reset and fold, quantiser).  The replays are checked
+kernels, combine, the library's amax clear and fold, quantiser).  The replays are checked
 bit for bit against the same calls made eagerly on the same inputs, with new
 inputs written between replays, and the first replay against the oracle."""
 import ctypes
@@ -91,7 +91,6 @@ class _Calls:
         F.fmha_decode_splitkv(self.qa, self.ka, self.va, self.oa, self.la, a["B"], a["Hq"],
                               a["Hkv"], 1, a["Sk"], a["D"], a["D"] ** -0.5, 0, a["ns"], self.wsa,
                               self.nba, None, stream=stream)
-        self.amax.zero_()  # a fill kernel on the current stream (no memset node)
         F.fmha_decode_splitkv(self.qb, self.kb, self.vb, self.ob, self.lb, b["B"], b["Hq"],
                               b["Hkv"], 1, b["Sk"], b["D"], b["D"] ** -0.5, 0, 0, self.wsb,
                               self.nbb, self.amax, stream=stream)
