@@ -39,6 +39,8 @@ SIGNATURES = {
                                        _SZ, _P, _P, _P, _P]),
     "fmha_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _I, _I, _F,
                                _I, _I, _P, _SZ, _P]),
+    "fmha_decode_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                                         _P, _P]),
     "fmha_decode_default_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fmha_decode_splitkv_dv_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fmha_decode_splitkv_dv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I,
@@ -131,6 +133,16 @@ def fmha_decode_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal, n
            lib.fmha_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq,
                                    Sk, D, float(scale), int(causal), int(num_splits),
                                    _ptr(workspace), int(workspace_bytes), _ptr(o_amax), st))
+
+
+def fmha_decode_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, scale, causal,
+                                num_splits, o_amax=None, stream=None):
+    lib = load_library()
+    st = stream if stream is not None else _stream(q.device)
+    _check("fmha_decode_splitkv_noalloc",
+           lib.fmha_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                           Hkv, Sq, Sk, D, float(scale), int(causal),
+                                           int(num_splits), _ptr(o_amax), st))
 
 
 def fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, Dv, num_splits) -> int:

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fmha.h"
 #include "fmha_device.hpp"
@@ -348,6 +349,79 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
   if (D == 576) return fail(FMHA_ERR_HEAD_DIM, "D = 576 needs Dv: use fmha_decode_splitkv_dv");
   return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, D, scale, causal, num_splits,
                      workspace, workspace_bytes, o_amax, nullptr, nullptr, nullptr, nullptr,
+                     stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split partials of fmha_decode_splitkv_noalloc: a fixed device array, one
+// copy per GPU, held until the process ends.  Its name is a host-side
+// stand-in in host code; kernels get the device address that
+// hipGetSymbolAddress returns for the current device (scratch_ptr).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current); null after a HIP error (recorded).
+void* scratch_ptr() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(FMHA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(FMHA_ERR_HIP, "device %d out of the supported range", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(FMHA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+fmha_status fmha_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                        float scale, int causal, int num_splits, float* o_amax,
+                                        void* stream) {
+  g_last_error[0] = 0;
+  // host-only checks first: nothing touches the device before they pass
+  fmha_status s = check_common(q, k, v, o, B, Hq, Hkv, Sq, Sk, scale, causal);
+  if (s != FMHA_OK) return s;
+  if (!decode_dim_ok(D))
+    return fail(FMHA_ERR_HEAD_DIM, "fmha_decode_splitkv_noalloc: D in {64, 128, 512}, got %d", D);
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(FMHA_ERR_ARG, "num_splits must be in 0..1024, got %d", num_splits);
+  const size_t need = fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D, num_splits);
+  if (need > kScratchBytes)
+    return fail(FMHA_ERR_WORKSPACE,
+                "fmha_decode_splitkv_noalloc: the split partials need %zu bytes, more than the "
+                "%zu bytes of its fixed scratch; use fewer splits or fmha_decode_splitkv",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr();
+    if (!ws) return FMHA_ERR_HIP;
+  }
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, D, scale, causal, num_splits, ws,
+                     need > 0 ? kScratchBytes : 0, o_amax, nullptr, nullptr, nullptr, nullptr,
                      stream);
 }
 

@@ -126,6 +126,31 @@ fmha_status fmha_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 int causal, int num_splits, void* workspace,
                                 size_t workspace_bytes, float* o_amax, void* stream);
 
+/*
+ * fmha_decode_splitkv for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the split partials in a fixed scratch
+ * array inside the library instead of a caller workspace.  Nothing is
+ * allocated and no workspace is passed; inputs and outputs are the caller's,
+ * as for fmha_decode_splitkv (same arguments without workspace /
+ * workspace_bytes, same results bit for bit).
+ *   Limit: fmha_decode_splitkv_workspace_size(B, Hq, Hkv, Sq, Sk, D,
+ *     num_splits) must not exceed 64 MiB (67108864 bytes); a larger request
+ *     returns FMHA_ERR_WORKSPACE before anything is launched (choose fewer
+ *     splits, or use fmha_decode_splitkv).  One split needs no scratch.
+ *   The scratch is 64 MiB of device memory on every GPU the library runs on,
+ *     held until the process ends; its address is looked up once per device
+ *     (the first call on that device, with it current).  Every call on one
+ *     GPU shares that GPU's scratch, so calls that overlap on one GPU (on
+ *     different streams, or from different threads without ordering) race
+ *     and may produce wrong results; calls ordered on one stream are safe.
+ *     Each call writes every partial it reads, so no clearing is needed.
+ */
+fmha_status fmha_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                        float scale, int causal, int num_splits, float* o_amax,
+                                        void* stream);
+
 /* The split count used when num_splits == 0. */
 int fmha_decode_default_splits(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 

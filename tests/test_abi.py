@@ -204,3 +204,22 @@ def test_debug_scores_validation():
     assert call(s=FAKE + 4) == 5
     assert call(decode=2) == 8
     assert call(D=192, Dv=128, v=FAKE) == 8               # V inside K: decode only
+
+
+def test_noalloc_validation_before_any_device_call():
+    """The no-allocation decode checks everything on the host, including that
+    its partials fit the fixed 64 MiB scratch, before touching the device."""
+    lib = F.load_library()
+    d = lib.fmha_decode_splitkv_noalloc
+
+    def call(q=FAKE, o=FAKE, B=32, Hq=64, Hkv=1, Sq=1, Sk=16384, D=512, ns=8, scale=0.04):
+        return d(q, FAKE, FAKE, o, None, B, Hq, Hkv, Sq, Sk, D, scale, 0, ns, None, None)
+
+    assert call(q=None) == 1
+    assert call(B=0) == 2
+    assert call(D=576) == 3 and call(D=16) == 3
+    assert call(Hq=3, Hkv=2) == 4
+    assert call(o=FAKE + 2) == 5
+    assert call(ns=-1) == 8 and call(ns=1025) == 8
+    assert call(ns=32) == 6   # 128 MiB of partials
+    assert b"64" in lib.fmha_last_error() or b"67108864" in lib.fmha_last_error()
