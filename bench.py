@@ -46,7 +46,8 @@ METRIC = "FMHA TFLOP/s (prefill) and KV GB/s (decode) at hd=64/512 on 1 MI355X"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["attn_kernels.hpp", "fmha_device.hpp", "launch.hpp", "fmha_prefill.hip",
                   "fmha_decode.hip", "nvfp4.hip", "nvfp4_device.hpp", "fmha_api.hip",
-                  "decode_launch.hpp", "fmha_decode_paged.hip", "fmha_debug.hip"]
+                  "decode_launch.hpp", "fmha_decode_paged.hip", "fmha_debug.hip",
+                  "prefill_kernel.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_workloads.md")
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_times_all_workloads.md")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s

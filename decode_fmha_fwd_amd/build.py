@@ -10,10 +10,10 @@ because it decides integer codes; the prefill kernels keep MFMA accumulators
 in ordinary VGPRs.
 
 The attention translation units issue some LDS reads from inline asm; their
-device assembly is kept from the compile (``-save-temps``) and checked by
-``asm_check`` before the library is linked, so a build in which register
-allocation touched such a read's result before its wait fails here instead of
-computing with stale data.
+device assembly (a device-only ``-S`` compile with the same flags, run beside
+the object compile) is checked by ``asm_check`` before the library is linked,
+so a build in which register allocation touched such a read's result before
+its wait fails here instead of computing with stale data.
 """
 from __future__ import annotations
 
@@ -70,32 +70,35 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [hipcc(), *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
-    tmp = None
-    if src in ASM_CHECKED:
-        tmp = os.path.join(BUILD, "temps_" + src.replace(".hip", ""))
-        shutil.rmtree(tmp, ignore_errors=True)
-        os.makedirs(tmp)
-        cmd.append("-save-temps")
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
+    r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    if tmp is not None:
-        asm = [f for f in os.listdir(tmp) if f.endswith(f"-hip-amdgcn-amd-amdhsa-{ARCH}.s")]
-        if len(asm) != 1:
-            raise RuntimeError(f"device assembly of {src} not found in {tmp}")
-        rep = asm_check.check_file(os.path.join(tmp, asm[0]))
-        if rep.problems:
-            raise RuntimeError(f"{src}: inline-asm LDS read hazard(s):\n" +
-                               "\n".join(rep.problems[:10]))
-        shutil.rmtree(tmp, ignore_errors=True)
     return obj
+
+
+def _check_asm(src: str) -> None:
+    """Device assembly of `src` (a device-only compile with the same flags),
+    checked for inline-asm LDS read hazards."""
+    asm = os.path.join(BUILD, src.replace(".hip", f"-{ARCH}.s"))
+    cmd = [hipcc(), *COMMON, *PER_FILE.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (device assembly) failed for {src}:\n{r.stderr}")
+    rep = asm_check.check_file(asm)
+    if rep.problems:
+        raise RuntimeError(f"{src}: inline-asm LDS read hazard(s):\n" + "\n".join(rep.problems[:10]))
+    os.remove(asm)
 
 
 def build(verbose: bool = False) -> str:
     """Compile all kernels and link libfmha.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(ASM_CHECKED)) as ex:
+        checks = [ex.submit(_check_asm, src) for src in sorted(ASM_CHECKED)]
         objs = list(ex.map(_compile, SOURCES))
+        for c in checks:
+            c.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -70,6 +70,8 @@ bool grid_fits(long long row_blocks, long long splits, long long Hkv, long long 
   return row_blocks * splits * Hkv * B < (1LL << 31);
 }
 
+}  // namespace
+
 int num_cus() {
   static int cus = [] {
     int dev = 0, n = 0;
@@ -80,6 +82,8 @@ int num_cus() {
   }();
   return cus;
 }
+
+namespace {
 
 // Clears the amax accumulator of a decode call (a kernel on the call's stream,
 // so the whole call can be captured in a graph).
@@ -148,6 +152,11 @@ fmha_status fwd_impl(const void* q, const void* k, const void* v, void* o, float
                 D, Dv);
   if (!sizes_fit(B, Hq, Hkv, Sq, Sk, D > Dv ? D : Dv))
     return fail(FMHA_ERR_SHAPE, "tensor too large");
+  // the prefill kernels address one head's K/V rows with 32-bit byte offsets
+  // (up to three tiles past the last key)
+  if (((long long)Sk + 4 * 64) * (D > Dv ? D : Dv) * 2 >= (1LL << 32))
+    return fail(FMHA_ERR_SHAPE, "Sk * head dim too large for the prefill (K/V rows of one head "
+                "must stay below 4 GiB)");
   AttnParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -165,8 +174,7 @@ fmha_status fwd_impl(const void* q, const void* k, const void* v, void* o, float
   p.splits_per_wg = 1;
   p.scale_log2 = scale * kLog2e;
   if (!grid_fits(p.n_row_blocks, 1, Hkv, B)) return fail(FMHA_ERR_SHAPE, "grid too large");
-  dim3 grid((unsigned)p.n_row_blocks * Hkv * B);
-  return launch_fwd(D, Dv, p, grid, causal != 0, (hipStream_t)stream);
+  return launch_fwd(D, Dv, p, causal != 0, (hipStream_t)stream);
 }
 
 }  // namespace

@@ -6,7 +6,7 @@
 // QK block under test is the one those kernels run.
 #include <hip/hip_runtime.h>
 
-#include "attn_kernels.hpp"
+#include "prefill_kernel.hpp"
 #include "host_common.hpp"
 #include "launch.hpp"
 
@@ -18,9 +18,7 @@ fmha_status launch_debug_scores(int D, int Dv, DecodeCfg c, const AttnParams& p,
   if (!decode) {
     s = with_fwd_cfg(D, Dv, [&](auto cfg) {
       using C = decltype(cfg);
-      hipLaunchKernelGGL((attn_fwd_kernel<C::D, C::MT, C::NW, C::KT, C::KS, C::VS, false, false,
-                                          false, false, C::DV, false, true>),
-                         grid, dim3(C::NW * 64), 0, st, p);
+      launch_prefill_cfg<C, false, true>(p, num_cus(), st);
       return check_launch("debug score launch (prefill)");
     });
   } else {

@@ -39,6 +39,7 @@ struct AttnParams {
   int bt_stride;
   int page_shift;          // log2(page_size); page_size is a power of two >= 64
   int num_pages;
+  int rb_per_wg;        // prefill: row blocks per workgroup (1, or 2 paired)
   // Test builds (DBG_S) only: raw score tiles times s_dbg_scale, [rows][Sk].
   float* s_dbg;
   float s_dbg_scale;
@@ -70,19 +71,22 @@ inline bool decode_groups_built(int D, int Dv, bool kv_shared) {
 }
 
 // Compile-time tile configuration of one attention kernel instantiation.
+// PIPE (prefill): the software-pipelined kernel of prefill_kernel.hpp (its
+// own fixed tiling) instead of attn_fwd_kernel.
 template <int D_, int MT_, int NW_, int KT_, int KS_, int VS_, bool KVS_ = false, int DV_ = D_,
-          bool GROUPS_ = false>
+          bool GROUPS_ = false, bool PIPE_ = false>
 struct TileCfg {
   static constexpr int D = D_, MT = MT_, NW = NW_, KT = KT_, KS = KS_, VS = VS_, DV = DV_;
-  static constexpr bool KVS = KVS_, GROUPS = GROUPS_;
+  static constexpr bool KVS = KVS_, GROUPS = GROUPS_, PIPE = PIPE_;
 };
 
 // The prefill kernel configurations (4 waves x 32 query rows, 64-key tiles):
 // calls f(TileCfg<...>{}) for the (D, Dv) pair and returns its status, or
-// FMHA_ERR_HEAD_DIM.  2-stage LDS rings at head dims 64 and 128 (3 stages at
-// 16 and 32; at 64 the 2-stage rings, 32 KB, measured 1-2 % faster than 3
-// stages, 48 KB, and 4 stages 5-8 % slower).  Q/K head dim 192 with V/O head
-// dim 128: 2-stage K (24 KB tiles) and V (16 KB) rings, 80 KB.
+// FMHA_ERR_HEAD_DIM.  Head dim 64: the pipelined kernel (4 waves x 32 rows,
+// 4-deep K and V rings, 64 KB, two workgroups per CU; 8 waves per workgroup
+// measured 7 % slower on the causal B4 H16 S2048 prefill).  attn_fwd_kernel elsewhere: 2-stage
+// LDS rings at head dim 128 (3 stages at 16 and 32); Q/K head dim 192 with
+// V/O head dim 128: 2-stage K (24 KB tiles) and V (16 KB) rings, 80 KB.
 template <class F>
 fmha_status with_fwd_cfg(int D, int Dv, F&& f) {
   if (D == 192 && Dv == 128) return f(TileCfg<192, 32, 4, 64, 2, 2, false, 128>{});
@@ -90,7 +94,7 @@ fmha_status with_fwd_cfg(int D, int Dv, F&& f) {
     switch (D) {
       case 16: return f(TileCfg<16, 32, 4, 64, 3, 3>{});
       case 32: return f(TileCfg<32, 32, 4, 64, 3, 3>{});
-      case 64: return f(TileCfg<64, 32, 4, 64, 2, 2>{});
+      case 64: return f(TileCfg<64, 32, 4, 64, 4, 4, false, 64, false, true>{});
       case 128: return f(TileCfg<128, 32, 4, 64, 2, 2>{});
     }
   }
@@ -122,9 +126,12 @@ fmha_status with_decode_cfg(int D, int Dv, DecodeCfg c, bool kv_shared, F&& f) {
   return FMHA_ERR_HEAD_DIM;
 }
 
-// fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows).
-fmha_status launch_fwd(int D, int Dv, const AttnParams& p, dim3 grid, bool causal,
-                       hipStream_t st);
+// Compute units of the current device (cached).
+int num_cus();
+
+// fmha_prefill.hip: 128-row prefill workgroups (4 waves x 32 rows); the
+// launcher sizes the grid (p.n_row_blocks row blocks of each unit).
+fmha_status launch_fwd(int D, int Dv, const AttnParams& p, bool causal, hipStream_t st);
 
 // fmha_decode.hip: split-KV decode (16-row waves) and the log-sum-exp combine.
 // D: head dim of Q/K, Dv: of V/O; kv_shared: V is the first Dv columns of the
@@ -136,6 +143,7 @@ fmha_status launch_decode_paged(int D, DecodeCfg c, const AttnParams& p, dim3 gr
                                 bool split, hipStream_t st);
 // fmha_debug.hip: the same prefill (decode = false) or one-split decode
 // kernels built with DBG_S (p.s_dbg, p.s_dbg_scale set), non-causal.
+// (prefill: the grid is sized by the launcher as for launch_fwd)
 fmha_status launch_debug_scores(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 grid,
                                 bool decode, bool kv_shared, hipStream_t st);
 fmha_status launch_combine(int D, const float* o_part, const float* lse_part, uint16_t* o,

@@ -223,3 +223,17 @@ def test_noalloc_validation_before_any_device_call():
     assert call(ns=-1) == 8 and call(ns=1025) == 8
     assert call(ns=32) == 6   # 128 MiB of partials
     assert b"64" in lib.fmha_last_error() or b"67108864" in lib.fmha_last_error()
+
+
+def test_library_has_no_undefined_symbols_of_its_own():
+    """Every kernel launched from host code has its host stub defined (a
+    missing stub only shows when the library is loaded for a call)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-C", "--undefined-only", F.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    own = [ln for ln in out.splitlines() if "fmha" in ln]
+    assert not own, own
