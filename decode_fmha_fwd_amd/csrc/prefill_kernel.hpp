@@ -104,6 +104,9 @@ void prefill_kernel(AttnParams p) {
   // and V(j+1) are copied in, and K(j) stays resident through iteration j
   // (the fast path's fallback recomputes its scores).
   constexpr int KST = 4, VST = 4;
+  // Tile t sits in ring stage (t - 1) & 3, so that iteration 1, where the
+  // steady-state loop starts, has phase 0 (see the loop below).
+  auto stage_of = [](int t) { return (t + 3) & 3; };
   constexpr int KTILE = KT * D, VTILE = KT * DV;
   using M = Mfma<32>;
   using Acc = f32x16;
@@ -194,23 +197,25 @@ void prefill_kernel(AttnParams p) {
     // copies, so every wait below is a constant count.
     // (the host keeps a head's K and V rows below 4 GiB, so the 32-bit buffer
     // offsets of every tile, and of the zero-filled tiles past the keys, fit)
-    auto issue_k = [&](int t) {
+    // (stage: t's ring stage, t & 3, passed in so that a compile-time
+    // constant reaches the LDS destination)
+    auto issue_k = [&](int t, int stage) {
       ck.issue(kbase, (uint32_t)kend * (D * 2), (uint32_t)t * (KT * D * 2),
-               (FMHA_LDS char*)&ksm[t & (KST - 1)][0], wave);
+               (FMHA_LDS char*)&ksm[stage][0], wave);
     };
-    auto issue_v = [&](int t) {
+    auto issue_v = [&](int t, int stage) {
       cv.issue(vbase, (uint32_t)kend * (DV * 2), (uint32_t)t * (KT * DV * 2),
-               (FMHA_LDS char*)&vsm[t & (VST - 1)][0], wave);
+               (FMHA_LDS char*)&vsm[stage][0], wave);
     };
 
     // Q first (the compiler's wait for it then leaves the copies in flight),
     // then the prologue copies K0 V0 K1 K2; iteration j issues K(j+3), V(j+1)
     bf16x8 qf[KSTEPS];
     load_q_frags<D, MT>(p.q + (row_base + my_rc) * D, kg, qf);
-    issue_k(0);
-    issue_v(0);
-    issue_k(1);
-    issue_k(2);
+    issue_k(0, stage_of(0));
+    issue_v(0, stage_of(0));
+    issue_k(1, stage_of(1));
+    issue_k(2, stage_of(2));
 
     // per-lane LDS offsets (constant over the loop; see attn_kernels.hpp)
     constexpr int KSW = CPR_LOG2<D / 8>::value;
@@ -249,7 +254,7 @@ void prefill_kernel(AttnParams p) {
     // QK product of tile t into S: K fragments read from LDS (asm) two
     // contraction steps ahead of the MFMAs that use them.
     auto qk = [&](int t, Acc (&S)[KBLK]) {
-      const uint32_t kst = k_lds + (uint32_t)(t & (KST - 1)) * (KTILE * 2);
+      const uint32_t kst = k_lds + (uint32_t)stage_of(t) * (KTILE * 2);
       constexpr int KRA = KSTEPS < 2 ? KSTEPS : 2;  // steps read ahead
       u32x4 kf[KSTEPS][KBLK];
       auto read = [&](auto s_c) {
@@ -280,7 +285,7 @@ void prefill_kernel(AttnParams p) {
     // PV product of tile t with packed P: V^T through transpose reads (asm),
     // RA units (one MFMA each) ahead of the MFMAs.
     auto pv = [&](int t, const u32x4 (&P)[NPV]) {
-      const uint32_t vst = v_lds + (uint32_t)(t & (VST - 1)) * (VTILE * 2);
+      const uint32_t vst = v_lds + (uint32_t)stage_of(t) * (VTILE * 2);
       constexpr int NU = NPV * DBLK;
       constexpr int RA = NU < 4 ? NU : 4;
       u32x4 vfrag[NU];
@@ -386,27 +391,34 @@ void prefill_kernel(AttnParams p) {
     // the fast softmax's bound test fails (as softmax_fast).
     // MASK: tile j crosses the causal diagonal or the ragged end; each score
     // past the lane row's last visible key gets p = 0 (see mask()).
-    auto full_interleaved = [&](auto mask_c, int j, Acc (&Sn)[KBLK], const u32x4 (&Pp)[NPV],
-                                Acc (&Sc)[KBLK], u32x4 (&Pc)[NPV]) {
+    // PH: the phase (j - 1) & 3 when known at compile time (the ring stages
+    // then travel as instruction immediates), else negative (stages from j at
+    // run time).  Stage of tile j + 1: PH + 1; of tile j - 1: PH - 1 (mod 4).
+    auto full_interleaved = [&](auto mask_c, auto ph_c, int j, Acc (&Sn)[KBLK],
+                                const u32x4 (&Pp)[NPV], Acc (&Sc)[KBLK], u32x4 (&Pc)[NPV]) {
       constexpr bool MASK = decltype(mask_c)::value;
+      constexpr int PH = decltype(ph_c)::value;
       const int d = lim - j * KT;
       static_assert(KSTEPS == 4 && KBLK == 2 && DBLK == 2, "the chunk plan is for D = DV = 64");
-      const uint32_t kst = k_lds + (uint32_t)((j + 1) & (KST - 1)) * (KTILE * 2);
-      const uint32_t vst = v_lds + (uint32_t)((j - 1) & (VST - 1)) * (VTILE * 2);
+      constexpr uint32_t kimm0 = PH >= 0 ? (uint32_t)((PH + 1) & 3) * (KTILE * 2) : 0u;
+      constexpr uint32_t vimm0 = PH >= 0 ? (uint32_t)((PH + 3) & 3) * (VTILE * 2) : 0u;
+      const uint32_t kst = k_lds + (PH >= 0 ? 0u : (uint32_t)stage_of(j + 1) * (KTILE * 2));
+      const uint32_t vst = v_lds + (PH >= 0 ? 0u : (uint32_t)stage_of(j - 1) * (VTILE * 2));
       u32x4 kf[KSTEPS][KBLK];
       u32x4 vfrag[8];
       auto read_k = [&](auto s_c) {
         constexpr int s_ = decltype(s_c)::value;
         static_for<0, KBLK>([&](auto kb_c) {
           constexpr int kb = decltype(kb_c)::value;
-          constexpr uint32_t imm = 2u * (kb * MT * D + (s_ / KPER) * KPER * 16);
+          constexpr uint32_t imm = kimm0 + 2u * (kb * MT * D + (s_ / KPER) * KPER * 16);
           kf[s_][kb] = lds_read_b128_imm<imm>(kst + koff[s_ % KPER]);
         });
       };
       auto read_v = [&](auto u_c) {
         constexpr int U = decltype(u_c)::value;
         constexpr int step = U / DBLK, db = U % DBLK;
-        constexpr uint32_t imm = step * (16u * DV * 2) + (uint32_t)(db / VPER) * VPER * MT * 2;
+        constexpr uint32_t imm =
+            vimm0 + step * (16u * DV * 2) + (uint32_t)(db / VPER) * VPER * MT * 2;
         const u32x2 lo = lds_read_tr16_imm<imm>(vst + voff0[db % VPER]);
         const u32x2 hi = lds_read_tr16_imm<imm>(vst + voff1[db % VPER]);
         vfrag[U] = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -492,15 +504,16 @@ void prefill_kernel(AttnParams p) {
     // Iteration j keeps S(j) in sbuf[j & 1] and P(j) in pbuf[j & 1]; the loops
     // below fix the parity at compile time everywhere, so no register copies
     // are needed between iterations.
-    auto sync = [&](int j) {
+    auto sync = [&](auto ph_c, int j) {
+      constexpr int PH = decltype(ph_c)::value;  // as for full_interleaved
       // K(j+1) and V(j-1) landed (the copies of iteration j-1 may still fly;
       // at j = 0, K(2) may), and every wave is past its reads of iteration j-1
       if (j == 0) wait_vmcnt<nK>();
       else wait_vmcnt<nK + nV>();
       wait_lgkmcnt0();
       lds_barrier();
-      issue_k(j + 3);
-      issue_v(j + 1);
+      issue_k(j + 3, PH >= 0 ? (PH + 3) & 3 : stage_of(j + 3));
+      issue_v(j + 1, PH >= 0 ? (PH + 1) & 3 : stage_of(j + 1));
     };
     // (the PV product of tile j-1 precedes the softmax of tile j in program
     // order: an exact-path rescale of O must apply to it, its P having been
@@ -509,13 +522,19 @@ void prefill_kernel(AttnParams p) {
     // MASK: the tile crosses the causal diagonal or the ragged end.  The last
     // iteration's QK(j+1) reads a zero-filled stage (its copy lay past the
     // keys) and is discarded.
-    auto full_iter = [&](auto par_c, auto mask_c, int j) {
-      constexpr int PAR = decltype(par_c)::value;  // j & 1
+    // ph_c: the phase (j - 1) & 3 (0 .. 3) when known at compile time, else
+    // -2 or -1: stages from j at run time, register buffers of parity 0 or 1
+    // (the buffer parity, which selects registers, is always a constant; it
+    // is j & 1 except where the masked iterations below renumber it).
+    auto full_iter = [&](auto ph_c, auto mask_c, int j) {
+      constexpr int PH = decltype(ph_c)::value;
+      constexpr int PAR = PH >= 0 ? ((PH + 1) & 1) : PH + 2;
       constexpr bool MASK = decltype(mask_c)::value;
-      sync(j);
+      sync(ph_c, j);
       bool ok;
       if constexpr (D == 64 && DV == 64) {
-        ok = full_interleaved(mask_c, j, sbuf[PAR ^ 1], pbuf[PAR ^ 1], sbuf[PAR], pbuf[PAR]);
+        ok = full_interleaved(mask_c, ph_c, j, sbuf[PAR ^ 1], pbuf[PAR ^ 1], sbuf[PAR],
+                              pbuf[PAR]);
       } else {
         qk(j + 1, sbuf[PAR ^ 1]);
         pv(j - 1, pbuf[PAR ^ 1]);
@@ -539,7 +558,7 @@ void prefill_kernel(AttnParams p) {
     // stand-in).  Every wave runs it (a tile past a wave's last visible key is
     // masked whole and adds nothing).
     if (ntiles > 0) {
-      sync(0);
+      sync(std::integral_constant<int, -2>{}, 0);
       if (1 < ntiles) {
         qk(1, sbuf[1]);
         dbg_store(sbuf[1], 1);
@@ -547,37 +566,50 @@ void prefill_kernel(AttnParams p) {
       if (0 >= n_clean) mask(sbuf[0], 0);
       softmax_exact(sbuf[0], pbuf[0]);
     }
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    // iterations 1 .. jm-1 need no mask, jm .. ntiles-1 do; the parity of j
-    // is a compile-time constant in every call
+    using Ph0 = std::integral_constant<int, 0>;
+    using Ph1 = std::integral_constant<int, 1>;
+    using Ph2 = std::integral_constant<int, 2>;
+    using Ph3 = std::integral_constant<int, 3>;
+    // Iterations 1 .. jm-1 need no mask: four at a time from j = 1 (phase 0)
+    // with every ring stage a compile-time constant, then up to three more
+    // (phases 0, 1, 2).  Iterations jm .. ntiles-1 (the causal diagonal and
+    // the ragged end, a few per row block) run with stages computed from j;
+    // they start with S(jm) in sbuf[0] and P(jm-1) in pbuf[1] (copied there
+    // when jm is odd), then alternate buffer parities.
     const int jm = max(1, min(ntiles, n_clean));
     int j = 1;
-    for (; j + 1 < jm; j += 2) {
-      full_iter(P1{}, NoMask{}, j);
-      full_iter(P0{}, NoMask{}, j + 1);
+    for (; j + 4 <= jm; j += 4) {
+      full_iter(Ph0{}, NoMask{}, j);
+      full_iter(Ph1{}, NoMask{}, j + 1);
+      full_iter(Ph2{}, NoMask{}, j + 2);
+      full_iter(Ph3{}, NoMask{}, j + 3);
     }
-    if (j < jm) {
-      full_iter(P1{}, NoMask{}, j);
-      ++j;
+    if (j < jm) full_iter(Ph0{}, NoMask{}, j++);
+    if (j < jm) full_iter(Ph1{}, NoMask{}, j++);
+    if (j < jm) full_iter(Ph2{}, NoMask{}, j++);
+    if (j < ntiles && (j & 1)) {  // renumber: S(j) -> sbuf[0], P(j-1) -> pbuf[1]
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb) sbuf[0][kb] = sbuf[1][kb];
+#pragma unroll
+      for (int st = 0; st < NPV; ++st) pbuf[1][st] = pbuf[0][st];
     }
-    if (j < ntiles && (j & 1)) {
-      full_iter(P1{}, Mask{}, j);
-      ++j;
-    }
+    const int jpar = j & 1;  // j's parity where the masked iterations start
     for (; j < ntiles; j += 2) {
-      full_iter(P0{}, Mask{}, j);
-      if (j + 1 < ntiles) full_iter(P1{}, Mask{}, j + 1);
+      full_iter(std::integral_constant<int, -2>{}, Mask{}, j);
+      if (j + 1 < ntiles) full_iter(std::integral_constant<int, -1>{}, Mask{}, j + 1);
     }
     // the last tile's PV product
     if (ntiles > 0) {
       wait_vmcnt<0>();
       wait_lgkmcnt0();
       lds_barrier();
+      // P(ntiles-1): in pbuf[(ntiles-1) & 1], or, when the masked iterations
+      // renumbered the buffers (started at an odd j), in the other one
       const int jl = ntiles - 1;
-      if (jl & 1) pv(jl, pbuf[1]);
+      const bool renumbered = jm < ntiles && jpar;
+      if (((jl & 1) ^ (renumbered ? 1 : 0)) != 0) pv(jl, pbuf[1]);
       else pv(jl, pbuf[0]);
     }
 
