@@ -56,8 +56,9 @@ PER_FILE = {
                   "-fno-gpu-flush-denormals-to-zero"],
 }
 SOURCES = ["fmha_api.hip", "fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip",
-           "fmha_debug.hip", "nvfp4.hip"]
-ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip", "fmha_debug.hip"}
+           "fmha_decode_wide.hip", "fmha_debug.hip", "nvfp4.hip"]
+ASM_CHECKED = {"fmha_prefill.hip", "fmha_decode.hip", "fmha_decode_paged.hip",
+               "fmha_decode_wide.hip", "fmha_debug.hip"}
 
 
 def hipcc() -> str:

@@ -304,9 +304,12 @@ fmha_status decode_impl(const void* q, const void* k, const void* v, void* o, fl
   // columns of the K rows, each key row is then streamed from HBM once and
   // serves both products
   const bool kv_shared = !pg && (k == v) && (D == 512 || Dv < D);
+  // (the wide-head kernel for V inside the K rows has no amax or NVFP4 epilogue)
+  const bool wide = !pg && !o_amax && !fp4_codes && decode_wide_takes(D, Dv, Sk, kv_shared);
   auto attention = [&](dim3 grid, bool split) {
-    return pg ? launch_decode_paged(D, c, p, grid, causal != 0, split, st)
-              : launch_decode(D, Dv, c, p, grid, causal != 0, split, kv_shared, st);
+    if (pg) return launch_decode_paged(D, c, p, grid, causal != 0, split, st);
+    if (wide) return launch_decode_wide(D, Dv, p, grid, causal != 0, split, false, st);
+    return launch_decode(D, Dv, c, p, grid, causal != 0, split, kv_shared, st);
   };
   if (ns_eff <= 1) {
     dim3 grid((unsigned)p.n_row_blocks * Hkv * B);

@@ -21,6 +21,8 @@ fmha_status launch_debug_scores(int D, int Dv, DecodeCfg c, const AttnParams& p,
       launch_prefill_cfg<C, false, true>(p, num_cus(), st);
       return check_launch("debug score launch (prefill)");
     });
+  } else if (decode_wide_takes(D, Dv, p.Sk, kv_shared)) {
+    s = launch_decode_wide(D, Dv, p, grid, false, false, true, st);
   } else {
     s = with_decode_cfg(D, Dv, c, kv_shared, [&](auto cfg) {
       using C = decltype(cfg);

@@ -55,9 +55,11 @@ def one_hot(B, Hq, Hkv, Sq, Sk, D, jstar, seed):
     return _bf16(q), _bf16(k), _bf16(v)
 
 
-def ramp(B, Hq, Hkv, Sq, Sk, D, seed, base=4.0):
+def ramp(B, Hq, Hkv, Sq, Sk, D, seed, base=4.0, kscale=1.0):
     """Row r of each head rises by base * alpha_r log2 units per 64 keys,
-    alpha_r spread over [0.5, 1.5]; two rows per head get 7.9 and 8.1 units."""
+    alpha_r spread over [0.5, 1.5]; two rows per head get 7.9 and 8.1 units.
+    kscale moves magnitude from the ramp column of K to that of Q (the same
+    scores), so that K stays of order 1 where it also serves as V."""
     g = _gen(seed)
     scale = default_scale(D)
     rows = Hq * Sq
@@ -66,10 +68,10 @@ def ramp(B, Hq, Hkv, Sq, Sk, D, seed, base=4.0):
         alpha[1] = 7.9 / base
         alpha[rows - 2] = 8.1 / base
     q = torch.randn((B, Hq, Sq, D), generator=g) * 0.1
-    q[..., 0] = alpha.view(Hq, Sq)
+    q[..., 0] = alpha.view(Hq, Sq) * kscale
     delta = base / (64.0 * scale * LOG2E)  # k[0] step per key for alpha = 1
     k = torch.randn((B, Hkv, Sk, D), generator=g)
-    k[..., 0] = torch.arange(Sk, dtype=torch.float32) * delta
+    k[..., 0] = torch.arange(Sk, dtype=torch.float32) * (delta / kscale)
     v = torch.randn((B, Hkv, Sk, D), generator=g)
     return _bf16(q), _bf16(k), _bf16(v)
 
@@ -235,3 +237,84 @@ def test_decode_causal_rows_with_fully_masked_splits(B, ns):
     v = _bf16(torch.randn((B, Hkv, Sk, D), generator=g))
     o, lse = run_decode(q, k, v, True, ns)
     check(q, k, v, True, o, lse, f"causal masked splits B={B}")
+
+
+# ------------------------------------------------------------------ V inside the K rows
+
+# B, Hq, Hkv, Sk, D, Dv, num_splits: V aliasing K at head dim 512, and V the
+# first 512 columns of 576-wide K rows (64 query rows per KV head: the
+# wide-head decode whose two waves per row group add their half-head-dim
+# score partials before the softmax)
+KVS_SHAPES = [
+    (1, 64, 1, 2100, 512, 512, 5),
+    (2, 64, 1, 2100, 576, 512, 3),
+]
+
+
+def run_decode_kvs(q, k, Dv, causal, ns):
+    dev = require_gpu()
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    qd, kd = q.to(dev), k.to(dev)
+    o = torch.full((B, Hq, Sq, Dv), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=dev)
+    nb = F.fmha_decode_splitkv_dv_workspace_size(B, Hq, Hkv, Sq, Sk, D, Dv, ns)
+    ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=dev)
+    F.fmha_decode_splitkv_dv(qd, kd, kd, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, default_scale(D),
+                             causal, ns, ws, nb)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_kvs(q, k, Dv, causal, o, lse, what):
+    return check(q, k, k[..., :Dv].contiguous(), causal, o, lse, what)
+
+
+@pytest.mark.parametrize("shape", KVS_SHAPES)
+@pytest.mark.parametrize("jstar", [2090, 1337])
+def test_decode_v_in_k_one_hot_score(shape, jstar):
+    B, Hq, Hkv, Sk, D, Dv, ns = shape
+    q, k, _ = one_hot(B, Hq, Hkv, 1, Sk, D, jstar, seed=jstar + 2)
+    o, lse = run_decode_kvs(q, k, Dv, False, ns)
+    o_ref, _ = check_kvs(q, k, Dv, False, o, lse, f"V in K, one-hot key {jstar} {shape}")
+    want = k[0, 0, jstar, :Dv].double().numpy()
+    assert np.abs(o_ref.reshape(B, Hq, Dv)[0, 0] - want).max() < 1e-12
+
+
+def ramp_small_k(B, Hq, Hkv, Sq, Sk, D, seed):
+    return ramp(B, Hq, Hkv, Sq, Sk, D, seed, kscale=1024.0)
+
+
+def large_scores_small_k(B, Hq, Hkv, Sq, Sk, D, seed):
+    """The score distribution of large_scores with all the magnitude in Q
+    (K, which is also V here, stays standard normal)."""
+    g = _gen(seed)
+    sig2 = 250.0 / (np.sqrt(D) * default_scale(D))
+    q = torch.randn((B, Hq, Sq, D), generator=g) * sig2
+    k = torch.randn((B, Hkv, Sk, D), generator=g)
+    return _bf16(q), _bf16(k), None
+
+
+@pytest.mark.parametrize("shape", KVS_SHAPES)
+@pytest.mark.parametrize("make", [ramp_small_k, large_scores_small_k, zero_q])
+def test_decode_v_in_k_ramp_large_and_closed_form(shape, make):
+    B, Hq, Hkv, Sk, D, Dv, ns = shape
+    q, k, _ = make(B, Hq, Hkv, 1, Sk, D, seed=19)
+    o, lse = run_decode_kvs(q, k, Dv, False, ns)
+    o_ref, _ = check_kvs(q, k, Dv, False, o, lse, f"V in K, {make.__name__} {shape}")
+    if make is zero_q:  # all scores 0: the mean of the V rows
+        want = k.double().numpy()[0, 0, :, :Dv].mean(axis=0)
+        assert np.abs(o_ref.reshape(B, Hq, Dv)[0, 0] - want).max() < 1e-12
+
+
+@pytest.mark.parametrize("D,Dv", [(512, 512), (576, 512)])
+def test_decode_v_in_k_causal_fully_masked_splits(D, Dv):
+    """Sq = 4 (64 rows per KV head with 16 heads), causal, Sk = 257 in splits
+    of 32 keys: the last split holds key 256 only, which only the last query
+    position sees."""
+    B, Hq, Hkv, Sq, Sk = 2, 16, 1, 4, 257
+    g = _gen(23)
+    q = _bf16(torch.randn((B, Hq, Sq, D), generator=g))
+    k = _bf16(torch.randn((B, Hkv, Sk, D), generator=g))
+    o, lse = run_decode_kvs(q, k, Dv, True, 9)
+    check_kvs(q, k, Dv, True, o, lse, f"V in K, causal masked splits D={D}")
