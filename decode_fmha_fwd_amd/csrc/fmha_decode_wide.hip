@@ -12,7 +12,7 @@ namespace {
 
 template <int D, int DV, bool C, bool S, bool DBG = false>
 fmha_status go(const AttnParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_wide_kernel<D, DV, C, S, DBG>), grid, dim3(512), 0, st, p);
+  hipLaunchKernelGGL((decode_wide_kernel<D, DV, C, S, DBG>), grid, dim3(kWideThreads), 0, st, p);
   return check_launch(DBG ? "debug score launch (wide decode)" : "wide decode launch");
 }
 

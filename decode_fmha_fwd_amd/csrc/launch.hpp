@@ -139,7 +139,7 @@ fmha_status launch_fwd(int D, int Dv, const AttnParams& p, bool causal, hipStrea
 fmha_status launch_decode(int D, int Dv, DecodeCfg c, const AttnParams& p, dim3 grid,
                           bool causal, bool split, bool kv_shared, hipStream_t st);
 // fmha_decode_wide.hip: the decode for V inside the K rows at head dims
-// 512/512 and 576/512 (8 waves, each holding half of the head dims; no amax
+// 512/512 and 576/512 (4 waves, each holding half of the head dims; no amax
 // or NVFP4 epilogue).  decode_wide_takes: whether it serves such a call;
 // dbg: the test-only score-storing build (non-causal, one split).
 bool decode_wide_takes(int D, int Dv, int Sk, bool kv_shared);
