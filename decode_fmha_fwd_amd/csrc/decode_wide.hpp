@@ -235,7 +235,11 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) oacc[i] = Acc{};
   float m_run = kNegBig;
-  float l_run = 0.0f;
+  // Row sums of P on the matrix cores: an extra MFMA per 16-key step with an
+  // all-ones A operand leaves every register of lane l holding the sum of
+  // its row's (bf16) probabilities, the very weights O accumulates.
+  Acc lacc = Acc{};
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const float c = p.scale_log2;
   Acc s_own = Acc{};  // this wave's QK partial of the tile the next iteration takes
 
@@ -362,8 +366,9 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
     }
     // ragged end and causal diagonal: key t0 + acc_row(lane, r) is visible
     // iff it is at most min(my_last, kend - 1); the row of register r is a
-    // constant plus 4 kg, so one compare per score
-    if ((t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last)) {
+    // constant plus 4 kg, so one compare per score.  (Without a causal mask
+    // only the last tile of a range can be ragged.)
+    if ((CAUSAL || !NEXT) && ((t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last))) {
       const int d = min(my_last, kend - 1) - t0 - 4 * kg;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
     // Softmax of S(t), in 16 slices placed between the MFMAs (base 2, lazy
     // rescale: m moves only when a row's tile maximum exceeds it by more than
     // kRescaleSlack).
-    float mloc = -__builtin_inff(), ps = 0.0f;
+    float mloc = -__builtin_inff();
     u32x4 pw[2];
     auto slice = [&](auto k_c) {
       constexpr int k = decltype(k_c)::value;
@@ -389,25 +394,20 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
           const float m_new = fmaxf(m_run, mloc);
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
-          l_run *= alpha;
+          scale_acc_agpr(lacc, alpha);
 #pragma unroll
           for (int i = 0; i < DBLK; ++i) scale_acc_agpr(oacc[i], alpha);
         }
       } else if constexpr (k <= 10) {
         constexpr int r0 = 2 * (k - 3);
 #pragma unroll
-        for (int r = r0; r < r0 + 2; ++r) {
-          sc[r] = fast_exp2(__builtin_fmaf(sc[r], c, -m_run));
-          ps += sc[r];
-        }
+        for (int r = r0; r < r0 + 2; ++r) sc[r] = fast_exp2(__builtin_fmaf(sc[r], c, -m_run));
       } else if constexpr (k <= 14) {
         // P as the B operand: k-slots 0..7 of 16-key step w/2 hold the S^T
         // registers 8 (w/2) + 0..7
         constexpr int w = k - 11;
         pw[w >> 1][2 * (w & 1)] = pack_bf16x2(sc[4 * w + 0], sc[4 * w + 1]);
         pw[w >> 1][2 * (w & 1) + 1] = pack_bf16x2(sc[4 * w + 2], sc[4 * w + 3]);
-      } else {
-        l_run += ps;
       }
     };
     if constexpr (!NEXT) static_for<0, 16>([&](auto k_c) { slice(k_c); });
@@ -436,6 +436,9 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
         const u32x4 vf = u32x4{vlo[U][0], vlo[U][1], vhi[U][0], vhi[U][1]};
         oacc[U % DBLK] = M::run(__builtin_bit_cast(bf16x8, vf),
                                 __builtin_bit_cast(bf16x8, pw[U / DBLK]), oacc[U % DBLK]);
+        if constexpr (U % DBLK == 0)  // the row sums of this 16-key step
+          lacc = M::run(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pw[U / DBLK]),
+                        lacc);
         // this wave's partial of S^T(t+1) for the partner, once the QK chain
         // has had a few MFMAs' time to finish
         if constexpr (NEXT && U == 3) {
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
   if constexpr (DBG_S) return;
 
   // ---- epilogue: this wave's half of O / l; lse from half 0 ----
-  const float l_tot = group_sum<32>(l_run);
+  const float l_tot = lacc[0];
   const bool empty = !(l_tot > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
