@@ -394,6 +394,11 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
           const float m_new = fmaxf(m_run, mloc);
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
+          // (the compiler puts no wait states between an MFMA and inline asm
+          // reading its result; the last MFMAs into lacc and oacc were issued
+          // in the previous iteration, before its last PV MFMAs, the barrier
+          // and the partial reads: far more than the 18 wait states an MFMA
+          // result needs)
           scale_acc_agpr(lacc, alpha);
 #pragma unroll
           for (int i = 0; i < DBLK; ++i) scale_acc_agpr(oacc[i], alpha);
