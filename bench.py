@@ -47,7 +47,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["attn_kernels.hpp", "fmha_device.hpp", "launch.hpp", "fmha_prefill.hip",
                   "fmha_decode.hip", "nvfp4.hip", "nvfp4_device.hpp", "fmha_api.hip",
                   "decode_launch.hpp", "fmha_decode_paged.hip", "fmha_debug.hip",
-                  "prefill_kernel.hpp"]
+                  "prefill_kernel.hpp", "buffer_copy.hpp", "decode_wide.hpp",
+                  "fmha_decode_wide.hip"]
+# the attention kernels (as opposed to the combine, quantiser and torch's fills)
+ATTENTION_KERNELS = ("attn_fwd_kernel", "prefill_kernel", "decode_wide_kernel")
+
+
+def is_attention_kernel(name: str) -> bool:
+    return any(a in name for a in ATTENTION_KERNELS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_all_workloads.md")
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_times_all_workloads.md")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
@@ -259,9 +266,13 @@ def kernel_source_sha() -> str:
 
 def headline_kernel(w) -> str:
     """A readable name of the workload's attention kernel."""
+    mask = "causal" if w.causal else "non-causal"
     if w.kind.startswith("fwd"):
-        return (f"attn_fwd_kernel<{w.D},32,4,64,{'causal' if w.causal else 'non-causal'}"
-                + (f",Dv={w.Dv}>" if w.Dv != w.D else ">"))
+        if w.D == 64 and w.Dv == 64:
+            return f"prefill_kernel<64,64,4 waves,{mask}> (pipelined)"
+        return f"attn_fwd_kernel<{w.D},32,4,64,{mask}" + (f",Dv={w.Dv}>" if w.Dv != w.D else ">")
+    if w.v_is_k and w.D >= 512:
+        return f"decode_wide_kernel<{w.D},{w.Dv}> (V inside the K rows)"
     return f"attn_fwd_kernel<{w.D},16,...> (decode)"
 
 
@@ -394,7 +405,7 @@ def trace_summary(path, steps, names):
             if len(d) < 2 * steps or k.startswith("void at::native"):
                 continue  # set-up work or the cache flush, not a timed kernel
             short = k if len(k) <= 110 else k[:107] + "..."
-            if "attn_fwd_kernel" in k:
+            if is_attention_kernel(k):
                 machine.append(f"trace_kernel_us_back_to_back {wname} "
                                f"{sum(d[-steps:]) / steps:.3f} sha {kernel_source_sha()}")
             for phase, dd in (("flushed", d[-2 * steps:-steps]), ("back-to-back", d[-steps:])):
@@ -438,7 +449,7 @@ def traffic_summary(w, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, calib
         short = k if len(k) <= 80 else k[:77] + "..."
         print(f"| {w.name} | `{short}` | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | "
               f"{rb / 1e6:.2f} | {wb / 1e6:.2f} | {w.bytes() / 1e6:.2f} |")
-        if "attn_fwd_kernel" in k:
+        if is_attention_kernel(k):
             main_bytes = int(rb + wb)
     if main_bytes is not None:
         print(f"traffic_bytes_per_launch {w.name} {main_bytes} sha {kernel_source_sha()}")
