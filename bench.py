@@ -239,7 +239,11 @@ def time_workload(w, dev, steps, warmup, settle_ms=0.0, inputs=None, flush=None)
     torch.cuda.synchronize()
     per_call = [a.elapsed_time(b) for a, b in ev]
     # 2. back-to-back: one event pair around K calls (an event between calls
-    #    would itself leave the GPU idle for a few microseconds per call)
+    #    would itself leave the GPU idle for a few microseconds per call),
+    #    after another untimed settle: right after the flushes the first
+    #    millisecond or so of compute-bound calls runs measurably slower
+    #    (the causal d64 prefill: 58.8 us per call over 30 calls, 47.5 over 200)
+    settle(r, settle_ms)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
