@@ -145,22 +145,19 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
 
   const int kbeg = split * p.split_len;
   int kend = min(Sk, kbeg + p.split_len);
-  int wave_min_last = INT_MAX, wave_max_last = INT_MAX;
   if (CAUSAL) {
     const int r_end = min(p.rows_per_kv, r_wg0 + 64) - 1;
     const int i_last = (r_wg0 / p.Sq == r_end / p.Sq) ? r_end % p.Sq : p.Sq - 1;
     kend = min(kend, i_last + diag + 1);
-    if (r_wave0 < p.rows_per_kv) {
-      const int rw_end = min(p.rows_per_kv, r_wave0 + 32) - 1;
-      const bool one_head = (r_wave0 / p.Sq == rw_end / p.Sq);
-      wave_min_last = (one_head ? r_wave0 % p.Sq : 0) + diag;
-      wave_max_last = (one_head ? rw_end % p.Sq : p.Sq - 1) + diag;
-    } else {
-      wave_min_last = wave_max_last = -1;
-    }
   }
   const int my_last = CAUSAL ? (my_rc % p.Sq) + diag : INT_MAX;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + KT - 1) / KT : 0;
+  // Tiles [0, n_clean) need a mask for no row: they end at or before kend and
+  // before every row's last visible key (row i sees keys up to i + diag,
+  // so at least up to diag).  Decode rows are few, so at most the last tile
+  // or two of a causal range need the mask.
+  const int lim_all = CAUSAL ? min(diag, kend - 1) : kend - 1;
+  const int n_clean = max(lim_all - kbeg + 1, 0) / KT;
 
   // ---- copies: the split's key rows, bounded (reads past kend return zeros)
   const uint16_t* kbase = p.k + ((long long)bh_kv * Sk + kbeg) * D;
@@ -279,9 +276,11 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
   }
 
   // ---- iteration t: S(t) from the partials, softmax, PV(t); with NEXT also
-  // the QK partial of tile t+1 and the copies of tile t+3 ----
-  auto iteration = [&](int t, auto next_c) {
+  // the QK partial of tile t+1 and the copies of tile t+3; with MASK the
+  // ragged end and the causal diagonal ----
+  auto iteration = [&](int t, auto next_c, auto mask_c) {
     constexpr bool NEXT = decltype(next_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     const int t0 = kbeg + t * KT;
     // Tile t+1 has landed (t+2 may still fly); every wave has written its
     // partial of S(t) and is past its reads of tile t-1 and of the partials
@@ -294,15 +293,6 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
     }
     wait_lgkmcnt0();
     lds_barrier();
-    // causal: tiles past the last visible key of this row group (and all
-    // later tiles) add nothing; the barriers and copies go on
-    if (CAUSAL && t0 > wave_max_last) {
-      if constexpr (NEXT) {
-        if constexpr (NXB == 1) lds_barrier();
-        issue_all(t + 3);
-      }
-      return;
-    }
     const int xb = (NXB == 2) ? (t & 1) : 0;
     const uint32_t vst = k_lds + (uint32_t)(t & 3) * (uint32_t)(KTILE * 2);
     const uint32_t kst = k_lds + (uint32_t)((t + 1) & 3) * (uint32_t)(KTILE * 2);
@@ -366,9 +356,9 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
     }
     // ragged end and causal diagonal: key t0 + acc_row(lane, r) is visible
     // iff it is at most min(my_last, kend - 1); the row of register r is a
-    // constant plus 4 kg, so one compare per score.  (Without a causal mask
-    // only the last tile of a range can be ragged.)
-    if ((CAUSAL || !NEXT) && ((t0 + KT > kend) || (CAUSAL && t0 + KT - 1 > wave_min_last))) {
+    // constant plus 4 kg, so one compare per score.  (A row with no visible
+    // key in the tile gets p = 0 throughout.)
+    if constexpr (MASK) {
       const int d = min(my_last, kend - 1) - t0 - 4 * kg;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -459,8 +449,10 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
     });
   };
 
-  for (int t = 0; t + 1 < ntiles; ++t) iteration(t, std::true_type{});
-  if (ntiles > 0) iteration(ntiles - 1, std::false_type{});
+  int t = 0;
+  for (; t + 1 < ntiles && t < n_clean; ++t) iteration(t, std::true_type{}, std::false_type{});
+  for (; t + 1 < ntiles; ++t) iteration(t, std::true_type{}, std::true_type{});
+  if (ntiles > 0) iteration(ntiles - 1, std::false_type{}, std::true_type{});
   // the copies past the last tile (zeros) land before the LDS is released
   wait_vmcnt<0>();
 

@@ -202,6 +202,7 @@ VK_CASES = [
     (1, 64, 1, 1, 300, 512, False, 1),
     (2, 32, 2, 1, 500, 512, False, 3),
     (1, 32, 1, 2, 400, 512, True, 2),
+    (1, 8, 1, 16, 700, 512, True, 3),   # Sq = 16 causal: two 64-row blocks, several masked tiles
     (2, 8, 2, 1, 300, 64, False, 2),    # other head dims take the two-ring path
 ]
 

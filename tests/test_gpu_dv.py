@@ -46,6 +46,7 @@ CASES = [
     (3, 8, 1, 1, 130, False, 2, False),    # 8 rows: a partly filled row block
     (2, 64, 4, 1, 1500, False, 0, True),   # 4 KV heads of 16 rows, heuristic splits
     (1, 16, 1, 3, 200, True, 2, False),    # three causal query rows (48 rows per KV head)
+    (1, 8, 1, 16, 700, True, 3, True),     # Sq = 16 causal, V inside K: two row blocks, masked tiles
 ]
 
 
