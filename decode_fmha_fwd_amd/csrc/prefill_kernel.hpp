@@ -619,6 +619,12 @@ void prefill_kernel(AttnParams p) {
     // row block's copies start after the barrier at its top.
     static_assert(DV == 64 && NW * MT * DV <= KST * KTILE, "O staging in the K ring");
     FMHA_LDS uint16_t* ost = (FMHA_LDS uint16_t*)&ksm[0][0] + wave * (MT * DV);
+    // (the lane index laundered through an empty asm, so the compiler does
+    // not hoist these addresses out of the row-block loop and hold them in
+    // registers through the main loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int oc = ln & 31, og = ln >> 5;  // = qcol, kg
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -628,13 +634,13 @@ void prefill_kernel(AttnParams p) {
         // 16-byte chunk db*4+qd of row qcol (columns 8 (db*4+qd) + 4 kg ..),
         // chunks XOR-swizzled by the row so the row-major reads below are
         // free of bank conflicts
-        const int cs = (db * 4 + qd) ^ (qcol & 7);
-        *(FMHA_LDS u32x2*)(ost + qcol * DV + cs * 8 + 4 * kg) = u32x2{w0, w1};
+        const int cs = (db * 4 + qd) ^ (oc & 7);
+        *(FMHA_LDS u32x2*)(ost + oc * DV + cs * 8 + 4 * og) = u32x2{w0, w1};
       }
     }
 #pragma unroll
     for (int i = 0; i < MT / 8; ++i) {  // (LDS accesses of one wave stay in order)
-      const int row = 8 * i + (lane >> 3), c = lane & 7;
+      const int row = 8 * i + (ln >> 3), c = ln & 7;
       const u32x4 val = *(FMHA_LDS u32x4*)(ost + row * DV + ((c ^ (row & 7)) * 8));
       if (r_wave0 + row < p.rows_per_kv)
         *(u32x4*)(p.o + (row_base + r_wave0 + row) * DV + c * 8) = val;
