@@ -232,11 +232,16 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) oacc[i] = Acc{};
   float m_run = kNegBig;
-  // Row sums of P on the matrix cores: an extra MFMA per 16-key step with an
-  // all-ones A operand leaves every register of lane l holding the sum of
-  // its row's (bf16) probabilities, the very weights O accumulates.
+  // Two row sums of P.  O is divided by the sum of the bf16-rounded P, the
+  // very weights it accumulates, so its weights sum to one; the matrix cores
+  // take it, an extra MFMA per 16-key step with an all-ones A operand leaving
+  // every register of lane l with its row's sum.  The log-sum-exp needs the
+  // sum of the unrounded p (with a few dominant keys the bf16 rounding moves
+  // it by up to 2-3e-3): the lane's fp32 partial sum, l_run.  (Dividing O by
+  // l_run instead raised its error to 2.3e-2 on such inputs.)
   Acc lacc = Acc{};
   const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float l_run = 0.0f;
   const float c = p.scale_log2;
   Acc s_own = Acc{};  // this wave's QK partial of the tile the next iteration takes
 
@@ -389,6 +394,7 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
           // in the previous iteration, before its last PV MFMAs, the barrier
           // and the partial reads: far more than the 18 wait states an MFMA
           // result needs)
+          l_run *= alpha;
           scale_acc_agpr(lacc, alpha);
 #pragma unroll
           for (int i = 0; i < DBLK; ++i) scale_acc_agpr(oacc[i], alpha);
@@ -396,7 +402,10 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
       } else if constexpr (k <= 10) {
         constexpr int r0 = 2 * (k - 3);
 #pragma unroll
-        for (int r = r0; r < r0 + 2; ++r) sc[r] = fast_exp2(__builtin_fmaf(sc[r], c, -m_run));
+        for (int r = r0; r < r0 + 2; ++r) {
+          sc[r] = fast_exp2(__builtin_fmaf(sc[r], c, -m_run));
+          l_run += sc[r];
+        }
       } else if constexpr (k <= 14) {
         // P as the B operand: k-slots 0..7 of 16-key step w/2 hold the S^T
         // registers 8 (w/2) + 0..7
@@ -431,7 +440,7 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
         const u32x4 vf = u32x4{vlo[U][0], vlo[U][1], vhi[U][0], vhi[U][1]};
         oacc[U % DBLK] = M::run(__builtin_bit_cast(bf16x8, vf),
                                 __builtin_bit_cast(bf16x8, pw[U / DBLK]), oacc[U % DBLK]);
-        if constexpr (U % DBLK == 0)  // the row sums of this 16-key step
+        if constexpr (U % DBLK == 0)  // the (bf16) row sums of this 16-key step
           lacc = M::run(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pw[U / DBLK]),
                         lacc);
         // this wave's partial of S^T(t+1) for the partner, once the QK chain
@@ -459,9 +468,10 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(AttnParams p)
   if constexpr (DBG_S) return;
 
   // ---- epilogue: this wave's half of O / l; lse from half 0 ----
-  const float l_tot = lacc[0];
+  const float l_bf = lacc[0];                 // divides O
+  const float l_tot = group_sum<32>(l_run);  // gives the log-sum-exp
   const bool empty = !(l_tot > 0.0f);
-  const float inv = empty ? 0.0f : 1.0f / l_tot;
+  const float inv = empty ? 0.0f : 1.0f / l_bf;
   const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
   if constexpr (SPLIT) {
     // The accumulators hold one row per lane, so stores straight from them

@@ -20,7 +20,11 @@ The cases:
   * scores of magnitude up to about 1000;
   * causal decode rows for which whole splits (all tiles of a split) are
     masked: with Sq = 4 and a last split holding only the last key, three of
-    the four rows see no key of that split (lse_s = -inf, weight 0).
+    the four rows see no key of that split (lse_s = -inf, weight 0);
+  * a few dominant keys: scores with a standard deviation of 3 or 4 (natural
+    log units), so a handful of keys carry each row's softmax and the bf16
+    rounding of P is most of the error -- the log-sum-exp must come from the
+    sum of the unrounded p (from the bf16 P it was off by up to 2.6e-3).
 """
 import numpy as np
 import pytest
@@ -127,6 +131,16 @@ def run_decode(q, k, v, causal, ns):
                           default_scale(D), causal, ns, ws, nb)
     torch.cuda.synchronize()
     return o, lse
+
+
+def few_dominant_keys(B, Hq, Hkv, Sq, Sk, D, seed, sd, Dv=None):
+    """Q scaled so that the scores scale * q.k have standard deviation sd."""
+    g = _gen(seed)
+    sig = sd / (np.sqrt(D) * default_scale(D))
+    q = torch.randn((B, Hq, Sq, D), generator=g) * sig
+    k = torch.randn((B, Hkv, Sk, D), generator=g)
+    v = torch.randn((B, Hkv, Sk, Dv or D), generator=g)
+    return _bf16(q), _bf16(k), _bf16(v)
 
 
 def check(q, k, v, causal, o, lse, what):
@@ -318,3 +332,35 @@ def test_decode_v_in_k_causal_fully_masked_splits(D, Dv):
     k = _bf16(torch.randn((B, Hkv, Sk, D), generator=g))
     o, lse = run_decode_kvs(q, k, Dv, True, 9)
     check_kvs(q, k, Dv, True, o, lse, f"V in K, causal masked splits D={D}")
+
+
+# ------------------------------------------------------------------ few dominant keys
+
+@pytest.mark.parametrize("sd", [3.0, 4.0])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 200, 64, True), (2, 4, 2, 300, 64, False),
+                                   (1, 4, 4, 200, 128, True)])
+def test_prefill_few_dominant_keys(shape, sd):
+    B, Hq, Hkv, S, D, causal = shape
+    q, k, v = few_dominant_keys(B, Hq, Hkv, S, S, D, seed=31, sd=sd)
+    o, lse = run_fwd(q, k, v, causal)
+    check(q, k, v, causal, o, lse, f"few dominant keys sd={sd} {shape}")
+
+
+@pytest.mark.parametrize("sd", [3.0, 4.0])
+@pytest.mark.parametrize("shape", [(4, 8, 2, 300, 64, 3), (4, 8, 8, 300, 128, 2),
+                                   (2, 16, 1, 300, 512, 2)])
+def test_decode_few_dominant_keys(shape, sd):
+    B, Hq, Hkv, Sk, D, ns = shape
+    q, k, v = few_dominant_keys(B, Hq, Hkv, 1, Sk, D, seed=37, sd=sd)
+    o, lse = run_decode(q, k, v, False, ns)
+    check(q, k, v, False, o, lse, f"few dominant keys sd={sd} {shape}")
+
+
+@pytest.mark.parametrize("sd", [3.0, 4.0])
+@pytest.mark.parametrize("shape", [(4, 64, 1, 40, 512, 512, 1), (4, 64, 1, 300, 512, 512, 2),
+                                   (4, 64, 1, 300, 576, 512, 2)])
+def test_decode_v_in_k_few_dominant_keys(shape, sd):
+    B, Hq, Hkv, Sk, D, Dv, ns = shape
+    q, k, _ = few_dominant_keys(B, Hq, Hkv, 1, Sk, D, seed=41, sd=sd)
+    o, lse = run_decode_kvs(q, k, Dv, False, ns)
+    check_kvs(q, k, Dv, False, o, lse, f"V in K, few dominant keys sd={sd} {shape}")
