@@ -276,7 +276,10 @@ fmha_status fmha_decode_paged(const void* q, const void* k_cache, const void* v_
  *   decode = 0: the prefill kernel fmha_fwd / fmha_fwd_dv would launch for
  *     (D, Dv) (32-row waves, 32x32x16 MFMAs); decode = 1: the one-split
  *     kernel fmha_decode_splitkv / _dv would launch (16-row waves, 16x16x32
- *     MFMAs), with v == k selecting the shared-ring form where that exists.
+ *     MFMAs), with v == k selecting the shared-ring form where that exists --
+ *     at (512, 512) and (576, 512) the wide-head decode (32-row waves, each
+ *     with half of the head dims, 32x32x16 MFMAs; the score of a pair is the
+ *     sum of its two halves' partials, as in that kernel).
  *   q, k, v: as for those calls; non-causal.
  *   s_out: fp32 [B * Hq * Sq, Sk] (row = (b * Hq + h) * Sq + i), every entry
  *     written; B * Hq * Sq * Sk < 2^31.
