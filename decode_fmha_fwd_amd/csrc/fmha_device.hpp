@@ -159,6 +159,15 @@ __device__ inline u32x2 lds_read_tr16_imm(uint32_t lds_addr) {
   return r;
 }
 
+// 16-byte global store that writes through the caches to memory and does not
+// keep the line (nt sc0 sc1: non-temporal, system scope).  For output read by
+// no later part of the kernel: written back during the kernel instead of by
+// the cache write-back at its end.  (gfx950 has no builtin that sets these
+// bits on a store; a plain store from asm, nothing waits on it.)
+__device__ inline void global_store_b128_stream(void* dst, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off nt sc0 sc1" ::"v"(dst), "v"(v) : "memory");
+}
+
 // 16-byte LDS read issued from inline asm, with a constant byte offset
 // folded into the instruction, for the same reason as the transpose reads: a
 // compiler-visible LDS read after asynchronous global->LDS copies makes the

@@ -642,8 +642,10 @@ void prefill_kernel(AttnParams p) {
     for (int i = 0; i < MT / 8; ++i) {  // (LDS accesses of one wave stay in order)
       const int row = 8 * i + (ln >> 3), c = ln & 7;
       const u32x4 val = *(FMHA_LDS u32x4*)(ost + row * DV + ((c ^ (row & 7)) * 8));
+      // (written through: 1.5-3 % faster than leaving 16 MB of O dirty in
+      // the L2s for the write-back at the kernel's end; same bits)
       if (r_wave0 + row < p.rows_per_kv)
-        *(u32x4*)(p.o + (row_base + r_wave0 + row) * DV + c * 8) = val;
+        global_store_b128_stream(p.o + (row_base + r_wave0 + row) * DV + c * 8, val);
     }
     if (row_ok && kg == 0 && p.lse) p.lse[row_base + my_r] = lse_val;
     }
