@@ -780,7 +780,55 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
   const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
 
   float amax = 0.0f;
-  if (row_ok) {
+  // 32-row waves (prefill) with whole 64-column blocks: O leaves the
+  // accumulators one row per lane in 8-byte pieces, so a store straight from
+  // them writes 16 bytes of each of 32 rows.  The wave's rows go row-major
+  // through the K ring, idle after the barrier below, and out as whole rows,
+  // 64 lanes x 16 bytes per store, written through (O is not left dirty in
+  // the L2s for the write-back at the kernel's end); 16-byte chunks
+  // XOR-swizzled by the row.
+  constexpr int OCH = DV / 8;  // 16-byte chunks per O row
+  constexpr bool kStageO = !SPLIT && MT == 32 && DV % 64 == 0 && OCH <= 64 &&
+                           NW * MT * DV <= KST * KTILE;
+  if constexpr (kStageO) {
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    lds_barrier();  // every wave past its last ring read
+    FMHA_LDS uint16_t* ost = (FMHA_LDS uint16_t*)&ksm[0][0] + wave * (MT * DV);
+    // (the lane index laundered through an empty asm, so that the compiler
+    // does not hoist these addresses out and hold them through the loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int oc = ln % MT, og = ln / MT;  // = qcol, kg
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float o0 = oacc[db][4 * qd + 0] * inv, o1 = oacc[db][4 * qd + 1] * inv;
+        const float o2 = oacc[db][4 * qd + 2] * inv, o3 = oacc[db][4 * qd + 3] * inv;
+        const uint32_t w0 = pack_bf16x2(o0, o1), w1 = pack_bf16x2(o2, o3);
+        const int cs = (db * 4 + qd) ^ (oc & (OCH - 1));
+        *(FMHA_LDS u32x2*)(ost + oc * DV + cs * 8 + 4 * og) = u32x2{w0, w1};
+        if (p.o_amax && row_ok) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 & 0xFFFF)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w0 >> 16)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 & 0xFFFF)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_float(w1 >> 16)));
+        }
+      }
+    }
+    if (p.o) {
+      constexpr int RPI = 64 / OCH;  // rows per store
+#pragma unroll
+      for (int i = 0; i < MT / RPI; ++i) {  // (LDS accesses of one wave stay in order)
+        const int row = RPI * i + ln / OCH, ch = ln % OCH;
+        const u32x4 val = *(FMHA_LDS u32x4*)(ost + row * DV + ((ch ^ (row & (OCH - 1))) * 8));
+        if (r_wave0 + row < p.rows_per_kv)
+          global_store_b128_stream(p.o + (row_base + r_wave0 + row) * DV + ch * 8, val);
+      }
+    }
+    if (row_ok && kg == 0 && p.lse) p.lse[row_base + my_r] = lse_val;
+  } else if (row_ok) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
