@@ -168,9 +168,12 @@ constexpr float kRescaleSlack = 8.0f;
 // each), 64/(DV/4) rows at a time; the combine kernel's 64 lanes, each with
 // the splits s = lane mod 64, are emulated by 64/(DV/4) "virtual lanes" per
 // lane, whose sums meet in the same tree order as its cross-lane butterfly.
-template <int DV>
-__device__ inline void combine_wave_rows(const float* __restrict__ o_part,
-                                         const float* __restrict__ lse_part, uint16_t* o,
+// PP: pointer to the partials (global, or LDS); prow0: the partial row of
+// output row row0.
+__device__ inline f32x4 load_f32x4(const float* p) { return *(const f32x4*)p; }
+__device__ inline f32x4 load_f32x4(const FMHA_LDS float* p) { return *(const FMHA_LDS f32x4*)p; }
+template <int DV, class PP>
+__device__ inline void combine_wave_rows(PP o_part, PP lse_part, long long prow0, uint16_t* o,
                                          float* lse, long long row0, int nrows, int nsplit,
                                          int lane) {
   static_assert(DV == 64 || DV == 128, "in-workgroup combine: head dims 64 and 128");
@@ -181,7 +184,8 @@ __device__ inline void combine_wave_rows(const float* __restrict__ o_part,
     const int r = r0 + lane / VL;
     const bool ok = r < nrows;
     const long long row = row0 + (ok ? r : 0);  // idle lanes repeat row0 (in bounds)
-    const float* lp = lse_part + row * nsplit;
+    const long long prow = prow0 + (ok ? r : 0);
+    const PP lp = lse_part + prow * nsplit;
     float m = -__builtin_inff();
     for (int s = li; s < nsplit; s += VL) m = fmaxf(m, lp[s]);
 #pragma unroll
@@ -209,12 +213,12 @@ __device__ inline void combine_wave_rows(const float* __restrict__ o_part,
       for (int k = 0; k < G; k += 2 * w) part[k] = part[k] + part[k + w];
     const float L = m + __logf(part[0]);
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const float* op = o_part + row * nsplit * DV + 4 * li;
+    const PP op = o_part + prow * nsplit * DV + 4 * li;
     int s = 0;
     for (; s + 4 <= nsplit; s += 4) {  // four splits' loads in flight, summed in order
       f32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = *(const f32x4*)(op + (long long)(s + u) * DV);
+      for (int u = 0; u < 4; ++u) x[u] = load_f32x4(op + (long long)(s + u) * DV);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float w = __expf(lp[s + u] - L);
@@ -223,7 +227,7 @@ __device__ inline void combine_wave_rows(const float* __restrict__ o_part,
     }
     for (; s < nsplit; ++s) {
       const float w = __expf(lp[s] - L);
-      acc += w * *(const f32x4*)(op + (long long)s * DV);
+      acc += w * load_f32x4(op + (long long)s * DV);
     }
     if (ok) {
       *(u32x2*)(o + row * DV + 4 * li) =
@@ -703,12 +707,45 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
     });
   };
 
+  // Split groups that combine in the workgroup may keep their partials in
+  // dynamic LDS instead of the workspace (the launch sizes it, when it leaves
+  // the workgroups of the grid resident at once): [row of the workgroup]
+  // [split][DV], then the lse values [row][split], for the first
+  // min(NW * MT, rows_per_kv) rows.  Through global memory the partial stores
+  // write 64 bytes of each of 16 rows per instruction between the splits'
+  // tiles, and the partials stay dirty in the L2s for the kernel-end
+  // write-back.
+  extern __shared__ __attribute__((aligned(16))) float part_lds[];
+  const bool plds = GROUP && p.part_lds_bytes > 0;
+  const int prows = min(ROWS_WG, p.rows_per_kv);
+
   // The split-s partial of this workgroup's rows: fp32 O / l and its lse.
   auto write_partial = [&](int s) {
     const float l_tot = group_sum<MT>(l_run);
     const bool empty = !(l_tot > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / l_tot;
     const float lse_val = empty ? -__builtin_inff() : (m_run + __log2f(l_tot)) * kLn2;
+    if (plds) {
+      if (row_ok) {
+        const int lr = my_r - r_wg0;
+        const uint32_t base = lds_addr((const FMHA_LDS void*)part_lds);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+          for (int qd = 0; qd < M::kRegs / 4; ++qd) {
+            const int d0 = (MT == 32) ? db * 32 + 8 * qd + 4 * kg : db * 16 + 4 * kg;
+            if (d0 >= DV) continue;
+            lds_write_b128_asm(base + 4u * (uint32_t)((lr * p.nsplit + s) * DV + d0),
+                               f32x4{oacc[db][4 * qd + 0] * inv, oacc[db][4 * qd + 1] * inv,
+                                     oacc[db][4 * qd + 2] * inv, oacc[db][4 * qd + 3] * inv});
+          }
+        }
+        if (kg == 0)
+          lds_write_b32_asm(base + 4u * (uint32_t)(prows * p.nsplit * DV + lr * p.nsplit + s),
+                            lse_val);
+      }
+      return;
+    }
     if (row_ok) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
@@ -764,9 +801,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnParams p) {
         if (p.combine_in_wg) {  // every split of the unit is here: combine in place
           __syncthreads();      // the partial stores of every lane are visible
           const int nr = min(MT, p.rows_per_kv - r_wave0);
-          if (nr > 0)
-            combine_wave_rows<DV>(p.o_part, p.lse_part, p.o, p.lse, row_base + r_wave0, nr,
-                                  p.nsplit, lane);
+          if (nr > 0) {
+            if (plds) {
+              const FMHA_LDS float* pl = (const FMHA_LDS float*)part_lds;
+              combine_wave_rows<DV>(pl, pl + prows * p.nsplit * DV, (long long)(r_wave0 - r_wg0),
+                                    p.o, p.lse, row_base + r_wave0, nr, p.nsplit, lane);
+            } else {
+              combine_wave_rows<DV>((const float*)p.o_part, (const float*)p.lse_part,
+                                    row_base + r_wave0, p.o, p.lse, row_base + r_wave0, nr,
+                                    p.nsplit, lane);
+            }
+          }
         }
       }
     } else {

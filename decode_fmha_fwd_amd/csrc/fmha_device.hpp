@@ -168,6 +168,17 @@ __device__ inline void global_store_b128_stream(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off nt sc0 sc1" ::"v"(dst), "v"(v) : "memory");
 }
 
+// LDS writes issued from inline asm: a compiler-visible LDS access while
+// asynchronous global->LDS copies are in flight makes the compiler wait for
+// all of them first (vmcnt(0)); these write a region no copy targets.  The
+// caller waits (lgkmcnt) before anything reads what they wrote.
+__device__ inline void lds_write_b128_asm(uint32_t lds_addr, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr), "v"(v) : "memory");
+}
+__device__ inline void lds_write_b32_asm(uint32_t lds_addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr), "v"(v) : "memory");
+}
+
 // 16-byte LDS read issued from inline asm, with a constant byte offset
 // folded into the instruction, for the same reason as the transpose reads: a
 // compiler-visible LDS read after asynchronous global->LDS copies makes the

@@ -31,6 +31,8 @@ struct AttnParams {
   int split_len;        // keys per range, a multiple of KT
   int splits_per_wg;    // consecutive splits one workgroup takes (split groups), >= 1
   int combine_in_wg;    // split groups holding every split: the kernel combines them
+  int part_lds_bytes;   // with combine_in_wg: > 0 when the partials stay in dynamic LDS
+                        // (that many bytes, [rows of the workgroup][nsplit][Dv + 1] fp32)
   float scale_log2;     // scale * log2(e)
   // Paged KV cache (decode only).  K and V are [num_pages][Hkv][page_size][D];
   // key j of batch b sits in page block_table[b * bt_stride + j / page_size].
