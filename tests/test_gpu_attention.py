@@ -269,7 +269,9 @@ def test_split_groups_equal_one_workgroup_per_split(B, Hq, Hkv, Sq, Sk, D, causa
     workgroups (here 512 units), one workgroup streams all splits of its unit
     and writes each split's partial: the arithmetic of one workgroup per
     split.  Batches of the grouped run must equal single-batch runs (too few
-    units to group) bit for bit, and the oracle."""
+    units to group) bit for bit, and the oracle.  The 1-wave cases keep the
+    partials in LDS (they fit beside the rings with every workgroup resident);
+    the 4-wave cases, whose partials would not, go through the workspace."""
     q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=D + Sq + B)
     scale = default_scale(D)
     o, lse = run_decode(q, k, v, scale, causal, ns)
