@@ -142,6 +142,22 @@ def test_prefill_causal_d64_workload():
     assert_parity(o, lse, o_ref, lse_ref, what=w.name)
 
 
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, S, causal: grids of two or more rounds of workgroup slots, where
+    # each head-dim-64 workgroup takes a heavy and a light row block in turn
+    (32, 16, 16, 384, True),    # 3 row blocks: one pair and one workgroup alone
+    (32, 32, 8, 300, True),     # GQA: 1200 rows per KV head, blocks span heads, last ragged
+    (32, 16, 16, 640, False),   # 5 row blocks, non-causal
+])
+def test_prefill_paired_row_blocks(case):
+    """Every output row against the oracle when row blocks are paired."""
+    B, Hq, Hkv, S, causal = case
+    q, k, v = make_qkv(B, Hq, Hkv, S, S, 64, seed=S + Hkv)
+    o, lse = run_fwd(q, k, v, default_scale(64), causal)
+    o_ref, lse_ref = oracle_rows(q, k, v, default_scale(64), causal)
+    assert_parity(o, lse, o_ref, lse_ref, what=str(case))
+
+
 def test_fwd_is_deterministic():
     q, k, v = make_qkv(1, 2, 2, 300, 300, 64, seed=3)
     o1, l1 = run_fwd(q, k, v, 0.125, True)
