@@ -278,6 +278,7 @@ def test_decode_amax_fold():
     (64, 32, 8, 2, 1000, 64, True, 8),     # causal, two query rows
     (64, 32, 8, 1, 1000, 128, False, 8),
     (256, 64, 2, 1, 300, 64, False, 4),    # 32 rows per KV head: 4-wave workgroups
+    (256, 48, 2, 1, 300, 64, False, 4),    # 24 rows: partials in LDS from two of four waves
     (256, 64, 2, 1, 300, 128, False, 3),
 ])
 def test_split_groups_equal_one_workgroup_per_split(B, Hq, Hkv, Sq, Sk, D, causal, ns):
@@ -285,9 +286,9 @@ def test_split_groups_equal_one_workgroup_per_split(B, Hq, Hkv, Sq, Sk, D, causa
     workgroups (here 512 units), one workgroup streams all splits of its unit
     and writes each split's partial: the arithmetic of one workgroup per
     split.  Batches of the grouped run must equal single-batch runs (too few
-    units to group) bit for bit, and the oracle.  The 1-wave cases keep the
-    partials in LDS (they fit beside the rings with every workgroup resident);
-    the 4-wave cases, whose partials would not, go through the workspace."""
+    units to group) bit for bit, and the oracle.  The 1-wave cases and the
+    24-row case keep the partials in LDS (they fit beside the rings with every
+    workgroup resident); the other 4-wave cases go through the workspace."""
     q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, D, seed=D + Sq + B)
     scale = default_scale(D)
     o, lse = run_decode(q, k, v, scale, causal, ns)
